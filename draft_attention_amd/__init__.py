@@ -1,0 +1,201 @@
+"""Python binding of libdraft_attn.so (MI355X draft-head decode attention).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/draft_attn.h. PyTorch supplies
+device memory and the current stream. There is no fallback: if the library is
+missing, importing the binding raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdraft_attn.so")
+
+FULL, WINDOW, FOLD = 0, 1, 2
+ROPE_NEOX, ROPE_NONE = 0, 1
+OK, EINVAL, ENOSPC, EHIP, ENOTSUP = 0, -1, -2, -3, -4
+MAX_ROWS = 32
+ABI_VERSION = 1
+_MODES = {"full": FULL, "window": WINDOW, "fold": FOLD}
+_ROPES = {"neox": ROPE_NEOX, "none": ROPE_NONE}
+
+
+class Params(ctypes.Structure):
+    """Mirror of draft_attn_params (field order and types must match the header)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_draft_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("n_sink", ctypes.c_int32),
+        ("n0", ctypes.c_int32),
+        ("rope", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("beta", ctypes.c_float),
+        ("kappa", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+        ("rope_theta", ctypes.c_double),
+        ("debug_visit", ctypes.c_void_p),
+        ("debug_visit_stride", ctypes.c_int64),
+        ("prof_events", ctypes.c_void_p * 2),
+        ("split_keys", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class DraftAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python -m draft_attention_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    lib.draft_attn_params_init.argtypes = [P]
+    lib.draft_attn_params_init.restype = None
+    lib.draft_attn_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.draft_attn_workspace_size.restype = ctypes.c_int
+    lib.draft_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.draft_attn_decode.restype = ctypes.c_int
+    lib.draft_attn_plan.argtypes = [P, i32p, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), i32p]
+    lib.draft_attn_plan.restype = ctypes.c_int
+    lib.draft_attn_strerror.argtypes = [ctypes.c_int]
+    lib.draft_attn_strerror.restype = ctypes.c_char_p
+    lib.draft_attn_version.argtypes = []
+    lib.draft_attn_version.restype = ctypes.c_int
+    if lib.draft_attn_version() != ABI_VERSION:
+        raise ImportError("libdraft_attn.so ABI version mismatch")
+    if ctypes.sizeof(Params) != 120:
+        raise ImportError("Params mirror has the wrong size")
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.draft_attn_strerror(int(status)).decode()
+
+
+def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                max_blocks_per_seq, mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0,
+                n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, split_keys=0,
+                debug_visit=0, debug_visit_stride=0, prof_events=None) -> Params:
+    p = Params()
+    lib.draft_attn_params_init(ctypes.byref(p))
+    p.num_seqs = int(num_seqs)
+    p.num_draft_tokens = int(num_draft_tokens)
+    p.num_q_heads = int(num_q_heads)
+    p.num_kv_heads = int(num_kv_heads)
+    p.head_dim = int(head_dim)
+    p.num_blocks = int(num_blocks)
+    p.max_blocks_per_seq = int(max_blocks_per_seq)
+    p.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
+    p.window = int(window)
+    p.n_sink = int(n_sink)
+    p.alpha = float(alpha)
+    p.beta = float(beta)
+    p.kappa = float(kappa)
+    p.n0 = int(n0)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim) if head_dim > 0 else 0.0
+    p.softmax_scale = float(softmax_scale)
+    p.rope = _ROPES[rope] if isinstance(rope, str) else int(rope)
+    p.rope_theta = float(rope_theta)
+    p.split_keys = int(split_keys)
+    p.debug_visit = int(debug_visit) or None
+    p.debug_visit_stride = int(debug_visit_stride)
+    if prof_events is not None:
+        p.prof_events[0] = int(prof_events[0])
+        p.prof_events[1] = int(prof_events[1])
+    return p
+
+
+def _host_i32(values):
+    arr = (ctypes.c_int32 * max(len(values), 1))(*[int(x) for x in values])
+    return arr
+
+
+def workspace_size(params: Params, ctx_lens) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib.draft_attn_workspace_size(ctypes.byref(params), _host_i32(ctx_lens), ctypes.byref(n))
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_workspace_size")
+    return int(n.value)
+
+
+def plan(params: Params, ctx_lens):
+    """Work items {seq, kv_head, key_begin, key_end, partition} and the chunk size."""
+    host = _host_i32(ctx_lens)
+    total = ctypes.c_int64(0)
+    chunk = ctypes.c_int32(0)
+    st = lib.draft_attn_plan(ctypes.byref(params), host, None, 0, ctypes.byref(total), ctypes.byref(chunk))
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_plan")
+    buf = (ctypes.c_int32 * (5 * max(total.value, 1)))()
+    st = lib.draft_attn_plan(ctypes.byref(params), host, buf, total.value, ctypes.byref(total),
+                             ctypes.byref(chunk))
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_plan")
+    items = [tuple(buf[5 * i:5 * i + 5]) for i in range(total.value)]
+    return items, int(chunk.value)
+
+
+def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
+           beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
+           ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
+           debug_visit=None, prof_events=None):
+    """Enqueue draft_attn_decode on the current (or given) stream; returns (out, lse).
+
+    q bf16 [B,T,Hq,d]; k_cache / k_side bf16 [NB,Hkv,16,d]; v_cache bf16 [NB,Hkv,d,16];
+    block_table int32 [B,MB]; ctx_len int32 [B] on the device; ctx_lens: the same
+    lengths as a host list (read from ctx_len when omitted, which synchronises).
+    out / lse / workspace are allocated with torch when not given.
+    """
+    import torch
+
+    B, T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if ctx_lens is None:
+        ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
+    visit_ptr, visit_stride = 0, 0
+    if debug_visit is not None:
+        visit_ptr, visit_stride = debug_visit.data_ptr(), debug_visit.shape[1]
+    p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                    num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
+                    window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
+                    softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
+                    split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
+                    prof_events=prof_events)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    need = workspace_size(p, ctx_lens)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    st = lib.draft_attn_decode(ctypes.byref(p), ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side),
+                               ptr(block_table), ptr(ctx_len), _host_i32(ctx_lens), ptr(out), ptr(lse),
+                               ptr(workspace), workspace.numel() * workspace.element_size(), s)
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_decode")
+    return out, lse

@@ -1,0 +1,674 @@
+// Draft-head decode attention over a paged KV cache: HIP kernels for CDNA4
+// (gfx950) and the draft_attn_decode entry point.
+//
+// Sources, by page title (sections in brackets):
+//   [WMTP] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
+//          Context" -- Abstract (full read vs sliding window plus sinks).
+//   [FOLD] "FOLD: Position-Free Far Memory with Local Order for Long-Context
+//          Speculative Decoding" -- summary and abstract (local window, far memory
+//          at one shared position from an unrotated side cache, decoupled softmax).
+//   [SD]   "SharpDraft: Accelerating Long-Context Speculative Decoding with
+//          Cardinality-Aware Query Scaling" -- Abstract (query scale by visible count).
+// The exact definitions this code computes are stated in include/draft_attn.h.
+//
+// Design. The call is bound by HBM: every visible key costs 4*d bytes of K and V
+// read once. Pass 1 splits the key axis of every (sequence, kv head) into work
+// items of C keys (plan.h); one 64-lane wave streams an item in steps of two
+// 16-token blocks (32 keys), keeping the whole GQA group x draft-token row set
+// (R <= 32 rows) of its kv head in registers, so each K/V byte is loaded by
+// exactly one wave:
+//   S^T[key][row] = K . Q^T   on v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q rows)
+//   online softmax per row    in the MFMA output layout: lane (row = l%16) holds
+//                             keys 4*(l/16)+r, so row statistics reduce with two
+//                             permlane swaps (lanes l^16, l^32)
+//   O^T[chan][row] += V^T . P^T  on the same MFMA: A = V^T comes straight from the
+//                             channel-major value block (one 16-byte load = 8
+//                             consecutive keys of one channel), B = P in bf16.
+// K and V fragments go from HBM to registers with 128-bit loads and no LDS
+// staging; the next step's loads are issued before the current step computes.
+// The key permutation inside a step is chosen so that the softmax output of the
+// Q.K^T product is already the B operand of the P.V product.
+// Pass 2 merges the per-item (max, sums, unnormalised output) records with the
+// log-sum-exp rule, then combines FOLD's local and far partitions with beta.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "host.h"
+#include "plan.h"
+
+namespace da {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxHalfDim = 64;
+
+struct Pass1Args {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* ks;
+  const int32_t* table;
+  const int32_t* ctx_len;
+  float4* stat;      // [items][rows_pad]: (max, denominator of acc, plain sum, 0), log2 domain
+  float* acc;        // [items][rows_pad][D]: unnormalised partial outputs
+  uint8_t* visit;    // optional [B][visit_stride]
+  int64_t visit_stride;
+  int32_t B, T, Hq, Hkv, G, R, rows_pad, max_blocks, num_blocks;
+  int32_t mode, W, S, n0, C, rope, total_items;
+  float alpha, kappa, scale;
+  double omega[kMaxHalfDim];  // RoPE frequencies rope_theta^(-2i/d)
+};
+
+struct Pass2Args {
+  const float4* stat;
+  const float* acc;
+  const int32_t* ctx_len;
+  float* out;
+  float* lse;
+  int32_t B, T, Hq, Hkv, G, R, rows_pad;
+  int32_t mode, W, S, C, total_items;
+  float alpha, beta;
+};
+
+// ---------------------------------------------------------------- lane helpers
+// permlane16/32 swaps return the pair {x[l], x[l^16]} (resp. l^32) in the two halves.
+__device__ __forceinline__ float pair_max16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_add16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_add32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Items of all sequences before sequence `b` (wave-wide prefix over ctx_len),
+// plus the per-kv-head item counts of `b`. Uniform across the wave.
+struct SeqInfo {
+  int32_t b, base, n, n_main;
+};
+
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Finds the sequence holding global item w; ok = false when w is past the
+// device-side item count.
+__device__ bool locate_item(int32_t w, const int32_t* __restrict__ ctx_len, int32_t B, int32_t Hkv,
+                            int32_t mode, int32_t W, int32_t S, int32_t C, SeqInfo* out) {
+  const int lane = threadIdx.x & 63;
+  int32_t acc = 0;
+  for (int32_t b0 = 0; b0 < B; b0 += 64) {
+    const int32_t b = b0 + lane;
+    int32_t cnt = 0, nm = 0;
+    if (b < B) cnt = seq_items(seq_ranges(ctx_len[b], mode, W, S), C, &nm) * Hkv;
+    const int32_t inc = wave_incl_scan(cnt, lane);
+    const int32_t total = __shfl(inc, 63, 64);
+    if (w < acc + total) {
+      const unsigned long long m = __ballot(acc + inc > w);
+      const int ln = __ffsll(m) - 1;
+      out->b = b0 + ln;
+      out->base = acc + __shfl(inc - cnt, ln, 64);
+      out->n = __shfl(cnt, ln, 64) / Hkv;
+      out->n_main = __shfl(nm, ln, 64);
+      return true;
+    }
+    acc += total;
+  }
+  return false;
+}
+
+// Prefix of item counts over sequences [0, b) and the counts of b.
+__device__ void seq_prefix(int32_t b, const int32_t* __restrict__ ctx_len, int32_t Hkv, int32_t mode,
+                           int32_t W, int32_t S, int32_t C, SeqInfo* out) {
+  const int lane = threadIdx.x & 63;
+  int32_t acc = 0;
+  for (int32_t b0 = 0; b0 < b; b0 += 64) {
+    const int32_t bb = b0 + lane;
+    int32_t cnt = 0;
+    if (bb < b) cnt = seq_items(seq_ranges(ctx_len[bb], mode, W, S), C, nullptr) * Hkv;
+    const int32_t inc = wave_incl_scan(cnt, lane);
+    acc += __shfl(inc, 63, 64);
+  }
+  int32_t nm = 0;
+  out->b = b;
+  out->base = acc;
+  out->n = seq_items(seq_ranges(ctx_len[b], mode, W, S), C, &nm);
+  out->n_main = nm;
+}
+
+// ---------------------------------------------------------------- pass 1
+template <int D>
+struct StepRegs {
+  bf16x8 k[2][D / 32];  // A operands of the two S^T key tiles, per k-step
+  bf16x8 v[D / 16];     // A operands of the O^T channel tiles
+  int32_t id0, id1;     // physical blocks of the step (-1: masked)
+};
+
+template <int D, int RT, bool FAR, bool LO>
+__device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* sbid, int32_t b, int32_t kvh,
+                                            int32_t kb, int32_t ke, int32_t part, int32_t w, float c2,
+                                            const bf16x8 (&qh)[RT][D / 32], const bf16x8 (&ql)[RT][D / 32]) {
+  constexpr int KS = D / 32, NT = D / 16;
+  const int lane = threadIdx.x, i16 = lane & 15, g = lane >> 4;
+  const __bf16* __restrict__ kpool = FAR ? a.ks : a.k;
+  const __bf16* __restrict__ vpool = a.v;
+  const int32_t blk0 = kb >> 4;
+  const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
+  const int32_t nsteps = (nblk + 1) >> 1;
+  // Key tile t of a step holds keys 8*(i>>2) + 4t + (i&3) at MFMA row i, so the
+  // S^T output lane (row, g) gets keys 8g..8g+3 (t=0) and 8g+4..8g+7 (t=1).
+  const int32_t kslot = 8 * ((i16 >> 2) & 1) + (i16 & 3);
+  const bool khi = (i16 >> 3) != 0;  // key tile rows 8..15 live in the step's second block
+  const bool vhi = (g >> 1) != 0;    // value keys 8g..8g+7 live in the second block for g >= 2
+  const bool sharp = FAR && (a.alpha != 1.f);
+  const float alpha = a.alpha;
+
+  float m[RT], l[RT], l1[RT];
+  f32x4 o[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.f;
+    l1[rt] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto issue = [&](int32_t s, StepRegs<D>& r) {
+    r.id0 = sbid[2 * s];
+    r.id1 = sbid[2 * s + 1];
+    int32_t kid = khi ? r.id1 : r.id0;
+    int32_t vid = vhi ? r.id1 : r.id0;
+    kid = kid < 0 ? 0 : kid;  // masked block: read block 0 (in bounds), values discarded
+    vid = vid < 0 ? 0 : vid;
+    const __bf16* kp = kpool + ((size_t)((int64_t)kid * a.Hkv + kvh) * 16 + kslot) * D + 8 * g;
+    const __bf16* vp = vpool + ((size_t)((int64_t)vid * a.Hkv + kvh) * D + i16) * 16 + 8 * (g & 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) r.k[t][ks] = *(const bf16x8*)(kp + t * 4 * D + ks * 32);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) r.v[n] = *(const bf16x8*)(vp + n * 256);
+  };
+
+  auto compute = [&](int32_t s, StepRegs<D>& r) {
+    const int32_t key0 = (blk0 + 2 * s) * 16;
+    const bool clean = key0 >= kb && key0 + 32 <= ke && r.id0 >= 0 && r.id1 >= 0;
+    // key (relative to key0) is scored iff its block is valid and it lies in [kb, ke)
+    auto key_ok = [&](int32_t rel) {
+      const int32_t id = rel >= 16 ? r.id1 : r.id0;
+      const int32_t key = key0 + rel;
+      return id >= 0 && key >= kb && key < ke;
+    };
+    if (a.visit != nullptr && lane < 32 && key_ok(lane))
+      a.visit[(int64_t)b * a.visit_stride + key0 + lane] = (uint8_t)(part + 1);
+    if (!clean) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!key_ok(8 * g + e)) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) r.v[n][e] = (__bf16)0.f;
+        }
+      }
+    }
+    // S^T tiles
+    f32x4 sc[2][RT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][ks], qh[rt][ks], c, 0, 0, 0);
+          if (LO) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][ks], ql[rt][ks], c, 0, 0, 0);
+        }
+        sc[t][rt] = c;
+      }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float xv = sc[t][rt][rr] * c2;
+          if (!clean && !key_ok(8 * g + 4 * t + rr)) xv = -INFINITY;
+          x[4 * t + rr] = xv;
+        }
+      float mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      mx = pair_max32(pair_max16(mx));
+      const float mnew = fmaxf(m[rt], mx);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float corr = ex2(m[rt] - mref);
+      bf16x8 pb;
+      float psum = 0.f;
+      if (sharp) {
+        const float corr_a = ex2(alpha * (m[rt] - mref));
+        float pasum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d0 = x[e] - mref;
+          const float p1 = ex2(d0);
+          const float pa = ex2(alpha * d0);
+          psum += p1;
+          pasum += pa;
+          pb[e] = (__bf16)pa;
+        }
+        l1[rt] = l1[rt] * corr + psum;
+        l[rt] = l[rt] * corr_a + pasum;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[rt][n] *= corr_a;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = ex2(x[e] - mref);
+          psum += p;
+          pb[e] = (__bf16)p;
+        }
+        l[rt] = l[rt] * corr + psum;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[rt][n] *= corr;
+      }
+      m[rt] = mnew;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[n], pb, o[rt][n], 0, 0, 0);
+    }
+  };
+
+  StepRegs<D> ra, rb;
+  issue(0, ra);
+  int32_t s = 0;
+  for (;;) {
+    if (s + 1 < nsteps) issue(s + 1, rb);
+    compute(s, ra);
+    if (++s >= nsteps) break;
+    if (s + 1 < nsteps) issue(s + 1, ra);
+    compute(s, rb);
+    if (++s >= nsteps) break;
+  }
+
+  // Row sums are lane-partial over the four key groups: reduce, then write.
+  const size_t rowbase = (size_t)w * a.rows_pad;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lsum = pair_add32(pair_add16(l[rt]));
+    const float l1sum = sharp ? pair_add32(pair_add16(l1[rt])) : lsum;
+    const int32_t row = 16 * rt + i16;
+    if (row < a.R) {
+      float* dst = a.acc + (rowbase + row) * D + 4 * g;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *(f32x4*)(dst + 16 * n) = o[rt][n];
+      if (g == 0) a.stat[rowbase + row] = make_float4(m[rt], lsum, l1sum, 0.f);
+    }
+  }
+}
+
+template <int D, int RT, bool FOLDK>
+__global__ __launch_bounds__(64) void pass1_kernel(const Pass1Args a) {
+  constexpr int KS = D / 32;
+  extern __shared__ int32_t sbid[];
+  const int lane = threadIdx.x, i16 = lane & 15, g = lane >> 4;
+  const int32_t w = blockIdx.x;
+  SeqInfo si;
+  if (!locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si)) {
+    // Only when ctx_len on the device disagrees with the host mirror: leave a
+    // neutral record so the merge stays defined.
+    if (lane < a.R) a.stat[(size_t)w * a.rows_pad + lane] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int32_t b = si.b;
+  const int32_t L = a.ctx_len[b];
+  const int32_t rel = w - si.base;
+  const int32_t kvh = rel / si.n, kidx = rel - kvh * si.n;
+  const Ranges rg = seq_ranges(L, a.mode, a.W, a.S);
+  int32_t kb, ke, part;
+  item_bounds(rg, kidx, a.C, &kb, &ke, &part);
+
+  // Block ids of the chunk, validated, plus one pad entry for the last step's pair.
+  const int32_t blk0 = kb >> 4;
+  const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
+  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  for (int32_t j = lane; j < nblk + 1; j += 64) {
+    int32_t id = -1;
+    if (j < nblk && blk0 + j < a.max_blocks) {
+      id = trow[blk0 + j];
+      if (id < 0 || id >= a.num_blocks) id = -1;
+    }
+    sbid[j] = id;
+  }
+  __syncthreads();
+
+  // Logit scale in the log2 domain: softmax_scale * s(n) * log2(e).
+  const int32_t n = visible_count(L, a.mode, a.W, a.S);
+  const double sn = 1.0 + (double)a.kappa * log((double)(n > a.n0 ? n : a.n0) / (double)a.n0);
+  const float c2 = (float)((double)a.scale * sn * 1.4426950408889634);
+
+  // Query rows of this kv head: row = t * G + (h - kvh * G), zero-padded to 16 * RT.
+  bf16x8 qh[RT][KS], ql[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int32_t row = 16 * rt + i16;
+    const bool ok = row < a.R;
+    const int32_t t = ok ? row / a.G : 0;
+    const int32_t head = kvh * a.G + (ok ? row - t * a.G : 0);
+    const __bf16* qp = a.q + ((int64_t)(b * a.T + t) * a.Hq + head) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+      qh[rt][ks] = ok ? *(const bf16x8*)(qp + 32 * ks) : z;
+      ql[rt][ks] = z;
+    }
+  }
+
+  if (FOLDK && part == kPartFar) {
+    if (a.rope == DRAFT_ATTN_ROPE_NEOX) {
+      // Far query q_far = R(-P_v) q, P_v = L - W - 1 [FOLD]. Lane (i16, g) holds
+      // channels 32ks + 8g + e; the rotation partner d/2 away sits in k-step
+      // ks + KS/2 of the same lane. Angles are formed and reduced mod 2*pi in fp64;
+      // the rotated value is split into bf16 hi + lo so the Q.K^T product keeps
+      // ~16 significant bits of q_far.
+      const double pv = (double)(L - a.W - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 32 * ks + 8 * g + e;
+          const double ang = -pv * a.omega[i];
+          const double kq = rint(ang * 0.15915494309189535);
+          double red = fma(-kq, 6.283185307179586, ang);
+          red = fma(-kq, 2.4492935982947064e-16, red);
+          float sn_, cs_;
+          sincosf((float)red, &sn_, &cs_);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const float x1 = (float)qh[rt][ks][e];
+            const float x2 = (float)qh[rt][ks + KS / 2][e];
+            const float y1 = x1 * cs_ - x2 * sn_;
+            const float y2 = x1 * sn_ + x2 * cs_;
+            const __bf16 h1 = (__bf16)y1, h2 = (__bf16)y2;
+            qh[rt][ks][e] = h1;
+            qh[rt][ks + KS / 2][e] = h2;
+            ql[rt][ks][e] = (__bf16)(y1 - (float)h1);
+            ql[rt][ks + KS / 2][e] = (__bf16)(y2 - (float)h2);
+          }
+        }
+      stream_item<D, RT, true, true>(a, sbid, b, kvh, kb, ke, part, w, c2, qh, ql);
+    } else {
+      stream_item<D, RT, true, false>(a, sbid, b, kvh, kb, ke, part, w, c2, qh, ql);
+    }
+  } else {
+    stream_item<D, RT, false, false>(a, sbid, b, kvh, kb, ke, part, w, c2, qh, ql);
+  }
+}
+
+// ---------------------------------------------------------------- pass 2
+// One workgroup of four waves per output row (sequence, kv head, query row):
+// the waves split the row's work items, keep running log-sum-exp records, and
+// wave 0 merges the four records and, for FOLD, the two partitions.
+template <int D>
+__global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
+  constexpr int CPL = D / 64;  // channels per lane
+  __shared__ float red_main[4][D + 2];
+  __shared__ float red_far[4][D + 3];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int32_t idx = blockIdx.x;
+  const int32_t row = idx % a.R;
+  const int32_t bh = idx / a.R;
+  const int32_t kvh = bh % a.Hkv;
+  const int32_t b = bh / a.Hkv;
+  SeqInfo si;
+  seq_prefix(b, a.ctx_len, a.Hkv, a.mode, a.W, a.S, a.C, &si);
+  int64_t i0 = (int64_t)si.base + (int64_t)kvh * si.n;
+  int64_t im = i0 + si.n_main;
+  int64_t i1 = i0 + si.n;
+  const int64_t lim = a.total_items;
+  i0 = i0 < lim ? i0 : lim;
+  im = im < lim ? im : lim;
+  i1 = i1 < lim ? i1 : lim;
+
+  float M = -INFINITY, Ls = 0.f, acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int64_t it = i0 + wv; it < im; it += 4) {
+    const size_t r = (size_t)it * a.rows_pad + row;
+    const float4 st = a.stat[r];
+    const float* src = a.acc + r * D + lane * CPL;
+    float v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = src[c];
+    if (st.x == -INFINITY) continue;
+    const float Mn = fmaxf(M, st.x);
+    const float so = exp2f(M - Mn), si_ = exp2f(st.x - Mn);
+    Ls = Ls * so + st.y * si_;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * so + v[c] * si_;
+    M = Mn;
+  }
+  float MF = -INFINITY, ZF = 0.f, ZFa = 0.f, accF[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) accF[c] = 0.f;
+  const float alpha = a.alpha;
+  for (int64_t it = im + wv; it < i1; it += 4) {
+    const size_t r = (size_t)it * a.rows_pad + row;
+    const float4 st = a.stat[r];
+    const float* src = a.acc + r * D + lane * CPL;
+    float v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = src[c];
+    if (st.x == -INFINITY) continue;
+    const float Mn = fmaxf(MF, st.x);
+    const float so = exp2f(MF - Mn), si_ = exp2f(st.x - Mn);
+    const float soa = exp2f(alpha * (MF - Mn)), sia = exp2f(alpha * (st.x - Mn));
+    ZF = ZF * so + st.z * si_;
+    ZFa = ZFa * soa + st.y * sia;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) accF[c] = accF[c] * soa + v[c] * sia;
+    MF = Mn;
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    red_main[wv][2 + lane * CPL + c] = acc[c];
+    red_far[wv][3 + lane * CPL + c] = accF[c];
+  }
+  if (lane == 0) {
+    red_main[wv][0] = M;
+    red_main[wv][1] = Ls;
+    red_far[wv][0] = MF;
+    red_far[wv][1] = ZF;
+    red_far[wv][2] = ZFa;
+  }
+  __syncthreads();
+  if (wv != 0) return;
+
+  M = -INFINITY;
+  Ls = 0.f;
+  MF = -INFINITY;
+  ZF = 0.f;
+  ZFa = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = accF[c] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float mk = red_main[k][0];
+    if (mk != -INFINITY) {
+      const float Mn = fmaxf(M, mk);
+      const float so = exp2f(M - Mn), si_ = exp2f(mk - Mn);
+      Ls = Ls * so + red_main[k][1] * si_;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * so + red_main[k][2 + lane * CPL + c] * si_;
+      M = Mn;
+    }
+    const float mf = red_far[k][0];
+    if (mf != -INFINITY) {
+      const float Mn = fmaxf(MF, mf);
+      const float so = exp2f(MF - Mn), si_ = exp2f(mf - Mn);
+      const float soa = exp2f(alpha * (MF - Mn)), sia = exp2f(alpha * (mf - Mn));
+      ZF = ZF * so + red_far[k][1] * si_;
+      ZFa = ZFa * soa + red_far[k][2] * sia;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) accF[c] = accF[c] * soa + red_far[k][3 + lane * CPL + c] * sia;
+      MF = Mn;
+    }
+  }
+
+  // log2 weights of the partitions; FOLD weighs the far memory by e^beta Z_F.
+  const float lwL = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
+  const float lwF = ZF > 0.f ? a.beta * kLog2e + MF + log2f(ZF) : -INFINITY;
+  const float top = fmaxf(lwL, lwF);
+  float res[CPL];
+  float lse_out;
+  if (top == -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) res[c] = 0.f;
+    lse_out = -INFINITY;
+  } else {
+    const float wL = exp2f(lwL - top), wF = exp2f(lwF - top);
+    const float den = wL + wF;
+    const float fl = wL > 0.f ? wL / (den * Ls) : 0.f;
+    const float ff = wF > 0.f ? wF / (den * ZFa) : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) res[c] = acc[c] * fl + accF[c] * ff;
+    lse_out = (top + log2f(den)) * kLn2;
+  }
+  const int32_t t = row / a.G;
+  const int32_t head = kvh * a.G + (row - t * a.G);
+  const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
+  float* dst = a.out + orow * D + lane * CPL;
+  if (CPL == 2) {
+    *(float2*)dst = make_float2(res[0], res[CPL - 1]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dst[c] = res[c];
+  }
+  if (lane == 0) a.lse[orow] = lse_out;
+}
+
+// ---------------------------------------------------------------- launch
+template <int D>
+static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t grid, size_t lds,
+                         hipStream_t s) {
+  if (row_tiles == 1) {
+    if (fold) pass1_kernel<D, 1, true><<<grid, 64, lds, s>>>(a);
+    else pass1_kernel<D, 1, false><<<grid, 64, lds, s>>>(a);
+  } else {
+    if (fold) pass1_kernel<D, 2, true><<<grid, 64, lds, s>>>(a);
+    else pass1_kernel<D, 2, false><<<grid, 64, lds, s>>>(a);
+  }
+}
+
+}  // namespace da
+
+extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
+                                 const void* v_cache, const void* k_side, const int32_t* block_table,
+                                 const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace da;
+  Prepared pr;
+  const int st = prepare(p, ctx_len_host, &pr);
+  if (st != DRAFT_ATTN_OK) return st;
+  if ((p->prof_events[0] == nullptr) != (p->prof_events[1] == nullptr)) return DRAFT_ATTN_EINVAL;
+  if (p->num_seqs == 0) return DRAFT_ATTN_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_len_dev || !out || !lse || !workspace)
+    return DRAFT_ATTN_EINVAL;
+  if ((p->mode == kFold) != (k_side != nullptr)) return DRAFT_ATTN_EINVAL;
+  auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
+  if (mis(q, 16) || mis(k_cache, 16) || mis(v_cache, 16) || (k_side && mis(k_side, 16)) ||
+      mis(out, 8) || mis(lse, 4) || mis(block_table, 4) || mis(ctx_len_dev, 4) || mis(workspace, 256))
+    return DRAFT_ATTN_EINVAL;
+  if (workspace_bytes < pr.workspace_bytes) return DRAFT_ATTN_ENOSPC;
+
+  const int D = p->head_dim;
+  char* ws = (char*)workspace;
+  Pass1Args a1;
+  a1.q = (const __bf16*)q;
+  a1.k = (const __bf16*)k_cache;
+  a1.v = (const __bf16*)v_cache;
+  a1.ks = (const __bf16*)k_side;
+  a1.table = block_table;
+  a1.ctx_len = ctx_len_dev;
+  a1.stat = (float4*)(ws + pr.stat_offset);
+  a1.acc = (float*)(ws + pr.acc_offset);
+  a1.visit = p->debug_visit;
+  a1.visit_stride = p->debug_visit_stride;
+  a1.B = p->num_seqs;
+  a1.T = p->num_draft_tokens;
+  a1.Hq = p->num_q_heads;
+  a1.Hkv = p->num_kv_heads;
+  a1.G = pr.G;
+  a1.R = pr.rows;
+  a1.rows_pad = pr.rows_pad;
+  a1.max_blocks = p->max_blocks_per_seq;
+  a1.num_blocks = p->num_blocks;
+  a1.mode = p->mode;
+  a1.W = p->window;
+  a1.S = p->n_sink;
+  a1.n0 = p->n0;
+  a1.C = pr.chunk;
+  a1.rope = p->rope;
+  a1.total_items = (int32_t)pr.total_items;
+  a1.alpha = p->alpha;
+  a1.kappa = p->kappa;
+  a1.scale = p->softmax_scale;
+  for (int i = 0; i < kMaxHalfDim; ++i)
+    a1.omega[i] = i < D / 2 ? pow(p->rope_theta, -2.0 * (double)i / (double)D) : 0.0;
+
+  Pass2Args a2;
+  a2.stat = a1.stat;
+  a2.acc = a1.acc;
+  a2.ctx_len = ctx_len_dev;
+  a2.out = out;
+  a2.lse = lse;
+  a2.B = a1.B;
+  a2.T = a1.T;
+  a2.Hq = a1.Hq;
+  a2.Hkv = a1.Hkv;
+  a2.G = a1.G;
+  a2.R = a1.R;
+  a2.rows_pad = a1.rows_pad;
+  a2.mode = a1.mode;
+  a2.W = a1.W;
+  a2.S = a1.S;
+  a2.C = a1.C;
+  a2.total_items = a1.total_items;
+  a2.alpha = p->alpha;
+  a2.beta = p->beta;
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a stale error so the check below reports ours
+  if (p->prof_events[0]) (void)hipEventRecord((hipEvent_t)p->prof_events[0], s);
+  if (pr.total_items > 0) {
+    const size_t lds = (size_t)(pr.chunk / 16 + 2) * sizeof(int32_t);
+    const bool fold = p->mode == kFold;
+    if (D == 64) launch_pass1<64>(a1, pr.row_tiles, fold, (uint32_t)pr.total_items, lds, s);
+    else launch_pass1<128>(a1, pr.row_tiles, fold, (uint32_t)pr.total_items, lds, s);
+  }
+  if (p->prof_events[1]) (void)hipEventRecord((hipEvent_t)p->prof_events[1], s);
+  const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
+  if (D == 64) pass2_kernel<64><<<rows_total, 256, 0, s>>>(a2);
+  else pass2_kernel<128><<<rows_total, 256, 0, s>>>(a2);
+  if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
+  return DRAFT_ATTN_OK;
+}

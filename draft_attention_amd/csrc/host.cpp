@@ -1,0 +1,170 @@
+// Host-side validation, chunk choice, workspace sizing and plan introspection.
+// See the header draft_attn.h for the argument contract.
+#include "host.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "plan.h"
+
+namespace da {
+
+namespace {
+
+// Aim for this many work items: a few per wave slot, so the split-K grid
+// fills the 256 compute units and finishes evenly.
+constexpr int64_t kTargetItems = 2048;
+constexpr int32_t kMinAutoChunk = 256;
+constexpr int32_t kMaxAutoChunk = 8192;
+constexpr int32_t kMaxChunk = 65536;
+constexpr int32_t kMaxLen = 1 << 30;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool finite_f(double x) { return isfinite(x) != 0; }
+
+}  // namespace
+
+int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* out) {
+  if (!p || !out) return DRAFT_ATTN_EINVAL;
+  if (p->struct_size != sizeof(draft_attn_params)) return DRAFT_ATTN_EINVAL;
+  if (p->reserved != 0) return DRAFT_ATTN_EINVAL;
+  const int32_t B = p->num_seqs, T = p->num_draft_tokens, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  if (B < 0 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DRAFT_ATTN_EINVAL;
+  if (p->block_size != kBlock) return DRAFT_ATTN_EINVAL;
+  if (p->head_dim < 1) return DRAFT_ATTN_EINVAL;
+  if (p->num_blocks < 0 || p->max_blocks_per_seq < 1) return DRAFT_ATTN_EINVAL;
+  if (p->mode != kFull && p->mode != kWindow && p->mode != kFold) return DRAFT_ATTN_EINVAL;
+  if (p->window < 0 || p->n_sink < 0 || p->window > kMaxLen || p->n_sink > kMaxLen) return DRAFT_ATTN_EINVAL;
+  if (p->mode == kFold && p->n_sink != 0) return DRAFT_ATTN_EINVAL;
+  if (p->n0 < 1) return DRAFT_ATTN_EINVAL;
+  if (p->rope != DRAFT_ATTN_ROPE_NEOX && p->rope != DRAFT_ATTN_ROPE_NONE) return DRAFT_ATTN_EINVAL;
+  if (!finite_f(p->alpha) || !(p->alpha > 0.f)) return DRAFT_ATTN_EINVAL;
+  if (!finite_f(p->beta) || !finite_f(p->kappa)) return DRAFT_ATTN_EINVAL;
+  if (!finite_f(p->softmax_scale) || !(p->softmax_scale > 0.f)) return DRAFT_ATTN_EINVAL;
+  if (p->mode == kFold && p->rope == DRAFT_ATTN_ROPE_NEOX &&
+      (!finite_f(p->rope_theta) || !(p->rope_theta > 0.0)))
+    return DRAFT_ATTN_EINVAL;
+  if (p->split_keys != 0 && (p->split_keys < 32 || p->split_keys > kMaxChunk || p->split_keys % 32 != 0))
+    return DRAFT_ATTN_EINVAL;
+  if (p->debug_visit && p->debug_visit_stride < 1) return DRAFT_ATTN_EINVAL;
+  if (B > 0 && !ctx_len_host) return DRAFT_ATTN_EINVAL;
+  if ((int64_t)p->max_blocks_per_seq * kBlock > (int64_t)kMaxLen * 2) return DRAFT_ATTN_EINVAL;
+
+  // Context lengths, query scale and the total key count.
+  int64_t keyheads = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t L = ctx_len_host[b];
+    if (L < 0 || L > kMaxLen) return DRAFT_ATTN_EINVAL;
+    if ((int64_t)L > (int64_t)p->max_blocks_per_seq * kBlock) return DRAFT_ATTN_EINVAL;
+    if (L > 0 && p->num_blocks < 1) return DRAFT_ATTN_EINVAL;
+    if (p->debug_visit && (int64_t)L > p->debug_visit_stride) return DRAFT_ATTN_EINVAL;
+    const int32_t n = visible_count(L, p->mode, p->window, p->n_sink);
+    const double s = 1.0 + (double)p->kappa * log((double)(n > p->n0 ? n : p->n0) / (double)p->n0);
+    if (!(s > 0.0)) return DRAFT_ATTN_EINVAL;
+    keyheads += (int64_t)n * Hkv;
+  }
+
+  // Kernel coverage of this build.
+  if (p->head_dim != 64 && p->head_dim != 128) return DRAFT_ATTN_ENOTSUP;
+  const int32_t G = Hq / Hkv;
+  const int64_t R = (int64_t)G * T;
+  if (R > DRAFT_ATTN_MAX_ROWS) return DRAFT_ATTN_ENOTSUP;
+
+  int32_t C = p->split_keys;
+  if (C == 0) {
+    const int64_t want = (keyheads + kTargetItems - 1) / kTargetItems;
+    C = kMinAutoChunk;
+    while (C < kMaxAutoChunk && C < want) C *= 2;
+  }
+
+  int64_t items = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const Ranges r = seq_ranges(ctx_len_host[b], p->mode, p->window, p->n_sink);
+    items += (int64_t)seq_items(r, C, nullptr) * Hkv;
+  }
+  if (items > 0x7fffffff) return DRAFT_ATTN_EINVAL;
+  if ((int64_t)B * Hkv * R > 0x7fffffff) return DRAFT_ATTN_EINVAL;
+
+  out->chunk = C;
+  out->total_items = items;
+  out->G = G;
+  out->rows = (int32_t)R;
+  out->row_tiles = (int32_t)((R + 15) / 16);
+  out->rows_pad = 16 * out->row_tiles;
+  const size_t nrows = (size_t)items * (size_t)out->rows_pad;
+  out->stat_offset = 0;
+  out->acc_offset = align_up(nrows * 4 * sizeof(float), 256);
+  out->workspace_bytes = align_up(out->acc_offset + nrows * (size_t)p->head_dim * sizeof(float), 256);
+  if (out->workspace_bytes == 0) out->workspace_bytes = 256;
+  return DRAFT_ATTN_OK;
+}
+
+}  // namespace da
+
+extern "C" {
+
+void draft_attn_params_init(draft_attn_params* p) {
+  if (!p) return;
+  memset(p, 0, sizeof(*p));
+  p->struct_size = sizeof(draft_attn_params);
+  p->block_size = 16;
+  p->mode = DRAFT_ATTN_FULL;
+  p->n0 = 1;
+  p->rope = DRAFT_ATTN_ROPE_NEOX;
+  p->alpha = 1.f;
+  p->beta = 0.f;
+  p->kappa = 0.f;
+  p->softmax_scale = 0.f;
+  p->rope_theta = 1e4;
+}
+
+int draft_attn_workspace_size(const draft_attn_params* p, const int32_t* ctx_len_host, size_t* bytes) {
+  if (!bytes) return DRAFT_ATTN_EINVAL;
+  da::Prepared pr;
+  const int st = da::prepare(p, ctx_len_host, &pr);
+  if (st != DRAFT_ATTN_OK) return st;
+  *bytes = pr.workspace_bytes;
+  return DRAFT_ATTN_OK;
+}
+
+int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t* items,
+                    int64_t capacity, int64_t* n_items, int32_t* chunk_keys) {
+  if (!n_items || capacity < 0) return DRAFT_ATTN_EINVAL;
+  da::Prepared pr;
+  const int st = da::prepare(p, ctx_len_host, &pr);
+  if (st != DRAFT_ATTN_OK) return st;
+  int64_t w = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const da::Ranges r = da::seq_ranges(ctx_len_host[b], p->mode, p->window, p->n_sink);
+    const int32_t n = da::seq_items(r, pr.chunk, nullptr);
+    for (int32_t h = 0; h < p->num_kv_heads; ++h) {
+      for (int32_t k = 0; k < n; ++k, ++w) {
+        if (items && w < capacity) {
+          int32_t kb, ke, part;
+          da::item_bounds(r, k, pr.chunk, &kb, &ke, &part);
+          int32_t* it = items + 5 * w;
+          it[0] = b; it[1] = h; it[2] = kb; it[3] = ke; it[4] = part;
+        }
+      }
+    }
+  }
+  *n_items = w;
+  if (chunk_keys) *chunk_keys = pr.chunk;
+  return DRAFT_ATTN_OK;
+}
+
+const char* draft_attn_strerror(int status) {
+  switch (status) {
+    case DRAFT_ATTN_OK: return "ok";
+    case DRAFT_ATTN_EINVAL: return "invalid argument";
+    case DRAFT_ATTN_ENOSPC: return "workspace too small";
+    case DRAFT_ATTN_EHIP: return "HIP launch error";
+    case DRAFT_ATTN_ENOTSUP: return "shape not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int draft_attn_version(void) { return DRAFT_ATTN_ABI_VERSION; }
+
+}  // extern "C"

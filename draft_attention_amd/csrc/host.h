@@ -1,0 +1,28 @@
+// Host-side validation and planning for draft_attn_decode. Pure C++: no HIP
+// headers, so the same file also builds with g++ for sanitizer runs.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/draft_attn.h"
+
+namespace da {
+
+struct Prepared {
+  int32_t chunk;          // C: keys per work item (multiple of 32)
+  int64_t total_items;    // work items over all sequences and kv heads
+  int32_t G;              // query heads per kv head
+  int32_t rows;           // R = G * T query rows per (sequence, kv head)
+  int32_t row_tiles;      // ceil(R / 16)
+  int32_t rows_pad;       // 16 * row_tiles
+  size_t stat_offset;     // workspace offset of the per-row statistics
+  size_t acc_offset;      // workspace offset of the per-row partial outputs
+  size_t workspace_bytes; // bytes the call needs
+};
+
+// Checks every scalar argument and the host context lengths, picks the chunk
+// size and sizes the workspace. Returns a DRAFT_ATTN_* status.
+int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* out);
+
+}  // namespace da

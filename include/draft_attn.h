@@ -1,0 +1,194 @@
+/*
+ * draft_attn.h -- C ABI of libdraft_attn.so: decode attention of a speculative
+ * draft head over a very long paged KV cache, on one AMD MI355X (gfx950).
+ *
+ * Sources (page titles; sections in brackets):
+ *   [WMTP] "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
+ *          Context" -- Abstract: a built-in draft head that attends over the whole
+ *          cache pays a read that grows with context; a sliding window plus
+ *          attention sinks on the draft only bounds that read. Its "Builds on"
+ *          list names PagedAttention, RoFormer and StreamingLLM.
+ *   [FOLD] "FOLD: Position-Free Far Memory with Local Order for Long-Context
+ *          Speculative Decoding" -- summary, review, abstract: a local window at
+ *          exact positions, all distant keys at one shared virtual position read
+ *          from an unrotated side cache, and a decoupled softmax with a
+ *          concentration factor alpha.
+ *   [SD]   "SharpDraft: Accelerating Long-Context Speculative Decoding with
+ *          Cardinality-Aware Query Scaling" -- Abstract: the query is scaled by a
+ *          closed-form, fixed-slope function of the number of visible keys.
+ *
+ * ---------------------------------------------------------------------------
+ * What one call computes. Notation: B sequences, L_b = ctx_len[b], T draft
+ * tokens per sequence, Hq query heads, Hkv kv heads, G = Hq / Hkv, head dim d.
+ * Query head h reads kv head h / G. All T draft tokens of a sequence attend to
+ * the same L_b cached keys and not to each other (merge draft-to-draft
+ * attention with the returned lse).
+ *
+ * 1. Visible sets, per mode:
+ *    DRAFT_ATTN_FULL    V = [0, L)                                   [WMTP]
+ *    DRAFT_ATTN_WINDOW  V = [0, min(n_sink, L)) U [max(0, L - W), L)  [WMTP]
+ *                       (W does not count the sinks; keys keep the rotation they
+ *                       were cached with -- the window masks, it does not re-index)
+ *    DRAFT_ATTN_FOLD    Loc = [max(0, L - W), L), Far = [0, max(0, L - W)) [FOLD]
+ *                       (no sinks: n_sink must be 0)
+ * 2. Query scale [SD]; the page prints no formula, this library fixes
+ *        s(n) = 1 + kappa * ln(max(n, n0) / n0),
+ *    n = |V| for FULL and WINDOW, n = L for FOLD. Logit scale
+ *    c = softmax_scale * s(n). kappa = 0 is the unmodified drafter. s(n) scales
+ *    fp32 logits, never the bf16 query, and needs no workspace.
+ * 3. Logits l_j = c * <q, k_j>, k_j from k_cache, over V (FULL, WINDOW) or Loc
+ *    (FOLD). FOLD far logits phi_j = c * <q_far, u_j>, u_j from k_side, with
+ *    q_far = R(-P_v) q and P_v = L - W - 1: every far key sits at the position
+ *    of the newest far key. R(a) is NeoX rotate-half RoPE: for i < d/2 the pair
+ *    (x_i, x_{i+d/2}) turns by a * rope_theta^(-2i/d) [WMTP, Builds on:
+ *    RoFormer]. DRAFT_ATTN_ROPE_NONE makes R the identity (NoPE drafters).
+ * 4. FULL, WINDOW:  lse = ln sum_V e^{l_j},  out = sum_V e^{l_j - lse} v_j.
+ * 5. FOLD decoupled softmax; the page prints no formula, this library fixes
+ *        Z_L = sum_Loc e^{l_j},  Z_F = sum_Far e^{phi_j},  Z_Fa = sum_Far e^{alpha phi_j}
+ *        lse = ln(Z_L + e^beta Z_F)
+ *        out = (sum_Loc e^{l_j} v_j + e^beta Z_F sum_Far (e^{alpha phi_j} / Z_Fa) v_j) / e^lse
+ *    alpha sharpens weights inside the far memory only; the far memory's total
+ *    weight against the window is e^beta Z_F / Z_L [FOLD, abstract]. alpha = 1,
+ *    beta = 0 is one softmax over Loc U Far.
+ * 6. An empty visible set gives out = 0 and lse = -inf.
+ *
+ * ---------------------------------------------------------------------------
+ * Layouts. All tensors are device memory owned by the caller; the library
+ * never retains, frees or allocates them.
+ *   q            bf16 [B][T][Hq][d], already RoPE-rotated by the caller at
+ *                its own positions. 16-byte aligned.
+ *   k_cache      bf16 [num_blocks][Hkv][16][d]: rotated keys; 16-token blocks,
+ *                slot-major (one key's d channels contiguous). 16-byte aligned.
+ *   v_cache      bf16 [num_blocks][Hkv][d][16]: values, channel-major inside a
+ *                block (one channel's 16 slots contiguous), so a 16-byte load
+ *                holds eight consecutive keys of one channel. 16-byte aligned.
+ *   k_side       bf16 [num_blocks][Hkv][16][d]: unrotated keys, same block ids
+ *                as k_cache; read for FOLD's far keys only. NULL unless FOLD.
+ *   block_table  int32 [B][max_blocks_per_seq]: key j of sequence b lives in
+ *                block block_table[b][j / 16], slot j % 16 [WMTP, Builds on:
+ *                PagedAttention]. Entries for blocks the mode never reads are
+ *                not read and may hold anything (e.g. -1); an entry that is read
+ *                and lies outside [0, num_blocks) is treated as a block of
+ *                masked keys (never dereferenced).
+ *   ctx_len_dev  int32 [B] on the device, read by the kernels;
+ *   ctx_len_host int32 [B] on the host, the same values, read for validation,
+ *                grid and workspace sizing. A mismatch gives wrong results but
+ *                no out-of-bounds access.
+ *   out          fp32 [B][T][Hq][d], written. 8-byte aligned.
+ *   lse          fp32 [B][T][Hq], natural log, written. 4-byte aligned.
+ *   workspace    device scratch of at least draft_attn_workspace_size() bytes,
+ *                256-byte aligned; its contents on entry do not matter.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t). The library allocates
+ * nothing, synchronises nothing and keeps no mutable global state: concurrent
+ * calls on different streams with distinct workspaces are safe.
+ *
+ * Errors: every check runs on the host before anything is enqueued, and a
+ * non-zero return means nothing was enqueued. DRAFT_ATTN_EHIP reports a launch
+ * failure seen by hipGetLastError() after enqueueing.
+ */
+#ifndef DRAFT_ATTN_H
+#define DRAFT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DRAFT_ATTN_ABI_VERSION 1
+
+/* modes */
+#define DRAFT_ATTN_FULL 0
+#define DRAFT_ATTN_WINDOW 1
+#define DRAFT_ATTN_FOLD 2
+
+/* rotary encoding of the FOLD far query */
+#define DRAFT_ATTN_ROPE_NEOX 0
+#define DRAFT_ATTN_ROPE_NONE 1
+
+/* status codes */
+#define DRAFT_ATTN_OK 0
+#define DRAFT_ATTN_EINVAL (-1)   /* bad argument, shape, pointer or alignment */
+#define DRAFT_ATTN_ENOSPC (-2)   /* workspace_bytes below draft_attn_workspace_size() */
+#define DRAFT_ATTN_EHIP (-3)     /* the HIP runtime reported a launch error */
+#define DRAFT_ATTN_ENOTSUP (-4)  /* valid, but this build has no kernel for it */
+
+/* Kernel support of this build: head_dim 64 or 128, block_size 16, and
+ * G * T <= DRAFT_ATTN_MAX_ROWS query rows per (sequence, kv head). */
+#define DRAFT_ATTN_MAX_ROWS 32
+
+typedef struct draft_attn_params {
+  uint32_t struct_size;        /* sizeof(draft_attn_params) */
+  int32_t num_seqs;            /* B >= 0 (0: nothing to do) */
+  int32_t num_draft_tokens;    /* T >= 1 */
+  int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;        /* Hkv >= 1 */
+  int32_t head_dim;            /* d: 64 or 128 */
+  int32_t block_size;          /* must be 16 */
+  int32_t num_blocks;          /* physical blocks in each pool */
+  int32_t max_blocks_per_seq;  /* row stride of block_table; 16 * it >= every L */
+  int32_t mode;                /* DRAFT_ATTN_FULL / _WINDOW / _FOLD */
+  int32_t window;              /* W >= 0 (WINDOW, FOLD; ignored by FULL) */
+  int32_t n_sink;              /* sinks >= 0 (WINDOW; must be 0 for FOLD; ignored by FULL) */
+  int32_t n0;                  /* SharpDraft reference count, >= 1 */
+  int32_t rope;                /* DRAFT_ATTN_ROPE_NEOX or _NONE (FOLD far query) */
+  float alpha;                 /* FOLD concentration factor, finite, > 0 */
+  float beta;                  /* FOLD far log-weight, finite */
+  float kappa;                 /* SharpDraft slope, finite, with s(n) > 0 for every n */
+  float softmax_scale;         /* finite, > 0; usually 1/sqrt(d) */
+  double rope_theta;           /* RoPE base, finite, > 0 (FOLD with NEOX) */
+  uint8_t* debug_visit;        /* optional device map [B][debug_visit_stride]: the kernel
+                                  writes 1 for each key scored from k_cache and 2 for
+                                  each key scored from k_side; untouched bytes keep
+                                  the caller's value. NULL: off (the fast path). */
+  int64_t debug_visit_stride;  /* >= max L when debug_visit is set */
+  void* prof_events[2];        /* optional hipEvent_t pair recorded on `stream` just
+                                  before and just after the streaming pass; NULL: off */
+  int32_t split_keys;          /* keys per work item: 0 = chosen by the library, else a
+                                  multiple of 32 in [32, 65536] */
+  int32_t reserved;            /* must be 0 */
+} draft_attn_params;
+
+/* Fill *p with defaults: FULL mode, block_size 16, alpha 1, beta 0, kappa 0,
+ * n0 1, NEOX with rope_theta 1e4, softmax_scale 0 (the caller sets it), all
+ * pointers NULL, struct_size set. Shapes stay 0. Never fails for non-NULL p. */
+void draft_attn_params_init(draft_attn_params* p);
+
+/* Workspace bytes that draft_attn_decode needs for these params and context
+ * lengths (host array of num_seqs entries). The size depends on shapes, mode,
+ * window, n_sink, split_keys and the lengths; it does not depend on alpha,
+ * beta or kappa. Returns DRAFT_ATTN_OK or the status draft_attn_decode would
+ * return for a validation failure. */
+int draft_attn_workspace_size(const draft_attn_params* p, const int32_t* ctx_len_host,
+                              size_t* bytes);
+
+/* Enqueue one decode-attention call (definitions above) on `stream`.
+ * q, k_cache, v_cache, k_side, block_table, ctx_len_dev, out, lse, workspace:
+ * device pointers; ctx_len_host: host pointer. k_side must be non-NULL exactly
+ * when mode is DRAFT_ATTN_FOLD. Returns a DRAFT_ATTN_* status. */
+int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
+                      const void* v_cache, const void* k_side, const int32_t* block_table,
+                      const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only introspection of the work decomposition a call would use: the
+ * chunk size in keys (*chunk_keys) and the work items in launch order, each
+ * {seq, kv_head, key_begin, key_end, partition} with partition 0 for keys read
+ * from k_cache and 1 for FOLD far keys read from k_side. Writes at most
+ * `capacity` items to `items` (may be NULL) and the total to *n_items. */
+int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t* items,
+                    int64_t capacity, int64_t* n_items, int32_t* chunk_keys);
+
+/* Static description of a status code. */
+const char* draft_attn_strerror(int status);
+
+/* DRAFT_ATTN_ABI_VERSION of the loaded library. */
+int draft_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRAFT_ATTN_H */

@@ -1,0 +1,219 @@
+"""Host side of the C ABI, on the CPU: exported symbols, the params struct
+layout, every validation path, and the work decomposition against the
+oracle's index sets. Nothing here launches a kernel."""
+
+import ctypes
+import os
+import random
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "draft_attn.h")
+
+
+def da():
+    import draft_attention_amd
+    return draft_attention_amd
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z][\w \*]*?\b(draft_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"draft_attn_decode", "draft_attn_workspace_size", "draft_attn_strerror",
+            "draft_attn_version", "draft_attn_plan", "draft_attn_params_init"} <= set(names)
+    lib = ctypes.CDLL(da().LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert da().lib.draft_attn_version() == 1
+
+
+def test_params_layout_matches_the_c_compiler(tmp_path):
+    fields = [f for f, _ in da().Params._fields_]
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void) {',
+             'printf("%zu\\n", sizeof(draft_attn_params));']
+    lines += [f'printf("%zu\\n", offsetof(draft_attn_params, {f}));' for f in fields]
+    lines += ['return 0; }']
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(da().Params)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(da().Params, f).offset == off, f
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert da().strerror(st) and da().strerror(st) != "unknown status"
+    assert da().strerror(-99) == "unknown status"
+
+
+# ----------------------------------------------------------------------------- validation
+BASE = dict(num_seqs=2, num_draft_tokens=4, num_q_heads=8, num_kv_heads=2, head_dim=128, num_blocks=64,
+            max_blocks_per_seq=32, mode="window", window=100, n_sink=4, n0=16)
+LENS = [300, 17]
+
+
+def call(params, lens=LENS, side=None, fold=False, ws_bytes=1 << 30, **ptrs):
+    """draft_attn_decode with fake, aligned device addresses: only reached code is host validation."""
+    P = dict(q=0x10000, k=0x20000, v=0x30000, ks=0x40000 if fold else None, table=0x50000, ctx=0x60000,
+             out=0x70000, lse=0x80000, ws=0x100000)
+    P.update(ptrs)
+    host = (ctypes.c_int32 * max(len(lens), 1))(*lens)
+    return da().lib.draft_attn_decode(ctypes.byref(params), P["q"], P["k"], P["v"], P["ks"], P["table"],
+                                      P["ctx"], host, P["out"], P["lse"], P["ws"], ws_bytes, None)
+
+
+def params(**kw):
+    d = dict(BASE)
+    d.update(kw)
+    return da().make_params(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=-1), -1), (dict(num_draft_tokens=0), -1), (dict(num_q_heads=7), -1),
+    (dict(num_kv_heads=0), -1), (dict(head_dim=96), -4), (dict(head_dim=0), -1),
+    (dict(num_q_heads=16, num_draft_tokens=5), -4),     # G*T = 40 rows > 32
+    (dict(mode=7), -1), (dict(window=-1), -1), (dict(n_sink=-2), -1),
+    (dict(mode="fold", n_sink=4), -1), (dict(n0=0), -1), (dict(rope=5), -1),
+    (dict(alpha=0.0), -1), (dict(alpha=-1.0), -1), (dict(alpha=float("inf")), -1),
+    (dict(beta=float("nan")), -1), (dict(kappa=float("inf")), -1), (dict(kappa=-10.0), -1),
+    (dict(softmax_scale=0.0), -1), (dict(softmax_scale=float("nan")), -1),
+    (dict(split_keys=48), -1), (dict(split_keys=16), -1), (dict(split_keys=1 << 20), -1),
+    (dict(max_blocks_per_seq=10), -1),                  # 160 keys < L = 300
+    (dict(num_blocks=0), -1),
+])
+def test_invalid_params_are_rejected_before_launch(kw, status):
+    fold = kw.get("mode") == "fold"
+    p = params(**kw)
+    assert call(p, fold=fold) == status
+    n = ctypes.c_size_t(0)
+    host = (ctypes.c_int32 * 2)(*LENS)
+    assert da().lib.draft_attn_workspace_size(ctypes.byref(p), host, ctypes.byref(n)) == status
+
+
+def test_struct_size_reserved_and_theta_checked():
+    p = params()
+    p.struct_size = 64
+    assert call(p) == -1
+    p = params()
+    p.reserved = 1
+    assert call(p) == -1
+    p = params(mode="fold", n_sink=0, rope_theta=0.0)
+    assert call(p, fold=True) == -1
+    p = params(mode="fold", n_sink=0, rope="none", rope_theta=0.0)   # theta unused without rotation
+    assert da().workspace_size(p, LENS) > 0
+
+
+def test_bad_lengths_pointers_and_alignment():
+    assert call(params(), lens=[-1, 5]) == -1
+    p = params()
+    assert da().lib.draft_attn_decode(ctypes.byref(p), 0x1000, 0x1000, 0x1000, None, 0x1000, 0x1000, None,
+                                      0x1000, 0x1000, 0x1000, 1 << 30, None) == -1   # no host lengths
+    for name in ("q", "k", "v", "table", "ctx", "out", "lse", "ws"):
+        assert call(params(), **{name: None}) == -1, name
+    assert call(params(), q=0x10008) == -1            # bf16 tensors need 16-byte alignment
+    assert call(params(), v=0x30004) == -1
+    assert call(params(), out=0x70004) == -1
+    assert call(params(), ws=0x100010) == -1
+    # k_side exactly when FOLD
+    assert call(params(), ks=0x40000) == -1
+    assert call(params(mode="fold", n_sink=0), fold=True, ks=None) == -1
+
+
+def test_workspace_too_small_and_prof_events():
+    p = params()
+    need = da().workspace_size(p, LENS)
+    assert call(p, ws_bytes=need - 1) == -2
+    p = params(prof_events=(0x1234, 0))
+    p.prof_events[1] = None
+    assert call(p) == -1
+
+
+def test_debug_visit_stride_checked():
+    p = params(debug_visit=0x9000, debug_visit_stride=100)
+    assert call(p) == -1          # L = 300 > stride
+
+
+def test_empty_batch_is_a_noop():
+    p = params(num_seqs=0)
+    assert call(p, lens=[]) == 0
+
+
+def test_workspace_independent_of_alpha_beta_kappa():
+    base = da().workspace_size(params(mode="fold", n_sink=0), LENS)
+    for kw in (dict(alpha=4.0), dict(beta=-3.0), dict(kappa=0.5), dict(alpha=0.1, beta=2.0, kappa=-0.1)):
+        assert da().workspace_size(params(mode="fold", n_sink=0, **kw), LENS) == base
+
+
+# ----------------------------------------------------------------------------- work decomposition
+def _check_plan(mode, W, S, lens, Hkv, split):
+    p = params(num_seqs=len(lens), num_kv_heads=Hkv, num_q_heads=Hkv * 2, num_draft_tokens=2, mode=mode,
+               window=W, n_sink=S, split_keys=split, max_blocks_per_seq=max(1, (max(lens) + 15) // 16),
+               num_blocks=1 << 20)
+    items, C = da().plan(p, lens)
+    assert C % 32 == 0 and (split == 0 or C == split)
+    seen = {}
+    prev = (-1, -1, -1)
+    for (b, h, kb, ke, part) in items:
+        assert 0 <= b < len(lens) and 0 <= h < Hkv and kb < ke and part in (0, 1)
+        assert kb // C == (ke - 1) // C, "chunk straddles a C boundary"
+        key = (b, h)
+        assert (b, h, part) >= prev, "launch order is sequence, kv head, partition"
+        prev = (b, h, part)
+        seen.setdefault((b, h, part), []).append((kb, ke))
+    for b, L in enumerate(lens):
+        main, far = oracle.index_sets(L, mode, W, S)
+        for h in range(Hkv):
+            for part, want in ((0, main), (1, far)):
+                got = np.concatenate([np.arange(kb, ke) for kb, ke in seen.get((b, h, part), [])] or
+                                     [np.zeros(0, dtype=np.int64)])
+                assert np.array_equal(np.sort(got), want), (b, h, part)
+                assert np.unique(got).size == got.size, "overlapping chunks"
+    n = ctypes.c_size_t(0)
+    assert da().workspace_size(p, lens) >= len(items) * 16 * (128 + 4) * 4
+
+
+def test_plan_covers_the_oracle_index_sets():
+    rnd = random.Random(0)
+    for _ in range(150):
+        mode = rnd.choice(["full", "window", "fold"])
+        lens = [rnd.choice([0, 1, 15, 16, 17, 31, 32, 33, rnd.randint(0, 5000)]) for _ in range(rnd.randint(1, 5))]
+        W = rnd.choice([0, 1, 16, 31, 100, 4096, rnd.randint(0, 3000)])
+        S = 0 if mode == "fold" else rnd.choice([0, 1, 4, 20, 100])
+        split = rnd.choice([0, 32, 64, 96, 256])
+        _check_plan(mode, W, S, lens, rnd.choice([1, 2, 8]), split)
+
+
+def test_auto_chunk_size_targets_the_workloads():
+    p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="full",
+               max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
+    items, C = da().plan(p, [1 << 20])
+    assert C == 4096 and len(items) == 2048
+    p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=4, mode="full",
+               max_blocks_per_seq=1 << 13, num_blocks=1 << 14)
+    items, C = da().plan(p, [131072])
+    assert C == 512 and len(items) == 2048
+
+
+def test_host_logic_under_sanitizers(tmp_path):
+    """host.cpp (validation + planner) built with g++ ASan/UBSan and fuzzed by a small driver."""
+    drv = os.path.join(ROOT, "tests", "host_fuzz.cpp")
+    src = os.path.join(ROOT, "draft_attention_amd", "csrc", "host.cpp")
+    exe = tmp_path / "host_fuzz"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-I", os.path.join(ROOT, "include"), drv, src, "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "ok" in res.stdout

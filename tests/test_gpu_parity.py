@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: max|d out| <= 1e-2 and max|d lse| <= 1e-3 for bf16 inputs with fp32
+accumulation; the set of keys each call scores (the debug visit map) must
+equal the oracle's index sets bit for bit. Inputs come from the seeded
+generator in ``synth``; unused pool slots are NaN, so any read outside the
+visible set poisons the result.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def _da():
+    import draft_attention_amd as da  # raises if the library is not built
+    return da
+
+
+def to_dev(x):
+    dev = torch.device("cuda:0")
+    return {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in x.items()}
+
+
+def np_inputs(x):
+    out = {}
+    for k, v in x.items():
+        if torch.is_tensor(v):
+            v = v.cpu()
+            out[k] = v.float().numpy() if v.is_floating_point() else v.numpy()
+        else:
+            out[k] = v
+    return out
+
+
+def expected_visit(ctx_lens, stride, mode, window=0, n_sink=0, **_):
+    m = np.zeros((len(ctx_lens), stride), dtype=np.uint8)
+    for b, L in enumerate(ctx_lens):
+        main, far = oracle.index_sets(L, mode, window, n_sink)
+        m[b, main] = 1
+        m[b, far] = 2
+    return m
+
+
+def run_gpu(g, kw, split=0, visit=True, theta=5e5, stream=None):
+    da = _da()
+    side = g["k_side"] if kw["mode"] == "fold" else None
+    vis = None
+    if visit:
+        stride = max(max(g["ctx_lens"]), 1)
+        vis = torch.zeros((len(g["ctx_lens"]), stride), dtype=torch.uint8, device="cuda:0")
+    out, lse = da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=side,
+                         ctx_lens=g["ctx_lens"], rope_theta=theta, split_keys=split, debug_visit=vis,
+                         stream=stream, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), (None if vis is None else vis.cpu().numpy())
+
+
+def compare(out, lse, ref, label, pairs=None, G=None):
+    if pairs is not None:
+        sel = np.zeros(ref["lse"].shape, dtype=bool)
+        for (b, g) in pairs:
+            sel[b, :, g * G:(g + 1) * G] = True
+        out, lse = out[sel], lse[sel]
+        rout, rlse = ref["out"][sel], ref["lse"][sel]
+    else:
+        rout, rlse = ref["out"], ref["lse"]
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    empty = np.isneginf(rlse)
+    assert np.array_equal(np.isneginf(lse), empty), f"{label}: empty-set rows differ"
+    dout = float(np.abs(out - rout).max()) if out.size else 0.0
+    dlse = float(np.abs(lse[~empty] - rlse[~empty]).max()) if (~empty).any() else 0.0
+    print(f"{label}: max|dout|={dout:.3e} max|dlse|={dlse:.3e}", flush=True)
+    assert dout <= OUT_TOL and dlse <= LSE_TOL, (label, dout, dlse)
+
+
+def check(x, kw, split=0, theta=5e5, label=""):
+    g = to_dev(x)
+    out, lse, vis = run_gpu(g, kw, split=split, theta=theta)
+    n = np_inputs(x)
+    ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"],
+                        k_side=n["k_side"], rope_theta=theta, **kw)
+    compare(out, lse, ref, label or str(kw))
+    want = expected_visit(x["ctx_lens"], vis.shape[1], **kw)
+    assert np.array_equal(vis, want), f"{label or kw}: visited key set differs from the oracle's"
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- small shapes
+def test_tiny_ctx4k_gqa4_d64_full_and_window():
+    w = synth.workloads()["tiny_4k_gqa4_d64"]
+    x = synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=0)
+    for kw in w.runs:
+        check(x, kw, theta=w.rope_theta, label=f"tiny {kw}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G,T", [(4, 4), (4, 8), (1, 1), (8, 3), (2, 5)])
+def test_full_and_window_shapes(d, G, T):
+    Hkv = 2
+    x = synth.make_inputs(ctx_lens=[1000, 37, 4097, 16], T=T, Hq=G * Hkv, Hkv=Hkv, d=d, seed=G * 10 + T)
+    for kw in (dict(mode="full"), dict(mode="window", window=300, n_sink=4),
+               dict(mode="window", window=0, n_sink=7), dict(mode="window", window=2000, n_sink=0)):
+        check(x, kw, label=f"d={d} G={G} T={T} {kw}")
+
+
+@pytest.mark.parametrize("rope", ["neox", "none"])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (2.0, 0.0), (4.0, -1.0), (0.5, 1.5)])
+def test_fold_modes(rope, alpha, beta):
+    x = synth.make_inputs(ctx_lens=[20000, 700, 4096, 4097, 5], T=6, Hq=16, Hkv=4, d=128, seed=5,
+                          fold=True, needle_frac=0.01)
+    kw = dict(mode="fold", window=4096, alpha=alpha, beta=beta, rope=rope)
+    check(x, kw, label=f"fold {kw}")
+
+
+def test_fold_small_window_and_zero_window():
+    x = synth.make_inputs(ctx_lens=[3000, 1, 64], T=2, Hq=4, Hkv=2, d=64, seed=8, fold=True)
+    for W in (0, 1, 17, 64):
+        check(x, dict(mode="fold", window=W, alpha=3.0, beta=-0.5), label=f"fold W={W}")
+
+
+def test_query_scaling_batched_ragged():
+    lens = [0, 1, 17, 5000, 33333, 4096, 12000]
+    x = synth.make_inputs(ctx_lens=lens, T=4, Hq=32, Hkv=8, d=128, seed=9, fold=True)
+    for kw in (dict(mode="full", kappa=0.1, n0=4096), dict(mode="window", window=1024, n_sink=4, kappa=0.3, n0=256),
+               dict(mode="fold", window=4096, alpha=2.0, beta=0.0, kappa=0.1, n0=4096),
+               dict(mode="full", kappa=-0.05, n0=16)):
+        check(x, kw, label=f"ragged {kw}")
+
+
+@pytest.mark.parametrize("split", [32, 64, 96, 512, 4096])
+def test_split_size_sweep(split):
+    x = synth.make_inputs(ctx_lens=[9000, 333], T=4, Hq=8, Hkv=2, d=128, seed=12, fold=True)
+    for kw in (dict(mode="full"), dict(mode="window", window=1000, n_sink=4),
+               dict(mode="fold", window=1000, alpha=2.0, beta=-1.0)):
+        check(x, kw, split=split, label=f"split={split} {kw}")
+
+
+def test_needles_full_attention():
+    x = synth.make_inputs(ctx_lens=[30000], T=8, Hq=32, Hkv=8, d=128, seed=13, needle_frac=0.01)
+    check(x, dict(mode="full"), label="needles full")
+    check(x, dict(mode="window", window=4096, n_sink=4), label="needles window")
+
+
+# ----------------------------------------------------------------------------- paging behaviour
+def test_unread_blocks_may_be_invalid():
+    # Blocks wholly outside the window are never read: give them -1 table entries.
+    L, W, S = 5000, 700, 4
+    x = synth.make_inputs(ctx_lens=[L], T=2, Hq=8, Hkv=2, d=128, seed=14)
+    kw = dict(mode="window", window=W, n_sink=S)
+    base, _ = check(x, kw)
+    t = x["block_table"].clone()
+    keep = set(range((S + 15) // 16)) | set(range((L - W) // 16, (L + 15) // 16))
+    for j in range(t.shape[1]):
+        if j not in keep:
+            t[0, j] = -1
+    y = dict(x, block_table=t)
+    out, _ = check(y, kw)
+    assert np.array_equal(out, base)
+
+
+def test_block_shuffle_gives_identical_results():
+    x = synth.make_inputs(ctx_lens=[3000, 50], T=4, Hq=8, Hkv=2, d=128, seed=15, fold=True)
+    NB = x["k_cache"].shape[0]
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(1))
+    inv = torch.argsort(perm)
+    t = x["block_table"]
+    t2 = torch.where(t >= 0, inv[t.clamp(min=0).long()].to(torch.int32), t)
+    y = dict(x, k_cache=x["k_cache"][perm], v_cache=x["v_cache"][perm], k_side=x["k_side"][perm],
+             block_table=t2)
+    for kw in (dict(mode="full"), dict(mode="fold", window=512, alpha=2.0, beta=-1.0)):
+        a, la = check(x, kw)
+        b, lb = check(y, kw)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_deterministic_and_stream_safe():
+    da = _da()
+    x = synth.make_inputs(ctx_lens=[8000, 900], T=4, Hq=16, Hkv=4, d=128, seed=16, fold=True)
+    g = to_dev(x)
+    kw = dict(mode="fold", window=1024, alpha=2.0, beta=-1.0)
+    a = run_gpu(g, kw)
+    b = run_gpu(g, kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for s, kw2 in ((s1, kw), (s2, dict(mode="full"))):
+        with torch.cuda.stream(s):
+            side = g["k_side"] if kw2["mode"] == "fold" else None
+            outs.append(da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"],
+                                  k_side=side, ctx_lens=g["ctx_lens"], rope_theta=5e5, **kw2))
+    torch.cuda.synchronize()
+    c = run_gpu(g, dict(mode="full"))
+    assert np.array_equal(outs[0][0].cpu().numpy(), a[0])
+    assert np.array_equal(outs[1][0].cpu().numpy(), c[0])
+
+
+def test_empty_batch_and_all_empty_sequences():
+    da = _da()
+    x = synth.make_inputs(ctx_lens=[0, 0], T=1, Hq=2, Hkv=1, d=64, seed=17)
+    g = to_dev(x)
+    out, lse = da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], ctx_lens=[0, 0])
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+def _sampled(w, kw, pairs, seed=0, theta=None):
+    """Full-size inputs generated on the GPU; the oracle runs on sampled (seq, kv head) pairs."""
+    dev = torch.device("cuda:0")
+    x = synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed, device=dev,
+                          fold=w.fold, needle_frac=w.needle_frac)
+    out, lse, vis = run_gpu(x, kw, visit=True, theta=w.rope_theta)
+    want = expected_visit(w.ctx_lens, vis.shape[1], **kw)
+    assert np.array_equal(vis, want)
+    heads = sorted({g for _, g in pairs})
+    G = w.Hq // w.Hkv
+    for g in heads:
+        # one kv head at a time: fp32 host copies of just that head's pools
+        sub = dict(q=x["q"][:, :, g * G:(g + 1) * G].float().cpu().numpy(),
+                   k=x["k_cache"][:, g:g + 1].float().cpu().numpy(),
+                   v=x["v_cache"][:, g:g + 1].float().cpu().numpy(),
+                   ks=None if x["k_side"] is None else x["k_side"][:, g:g + 1].float().cpu().numpy())
+        bsel = sorted({b for b, gg in pairs if gg == g})
+        ref = oracle.decode(sub["q"], sub["k"], sub["v"], x["block_table"].cpu().numpy(), w.ctx_lens,
+                            k_side=sub["ks"], rope_theta=w.rope_theta, pairs={(b, 0) for b in bsel}, **kw)
+        o = out[:, :, g * G:(g + 1) * G][bsel]
+        ls = lse[:, :, g * G:(g + 1) * G][bsel]
+        r = dict(out=ref["out"][bsel], lse=ref["lse"][bsel])
+        compare(o, ls, r, f"{w.name} {kw} kv={g} seqs={bsel}")
+        del sub
+
+
+def test_full_size_llama8b_128k():
+    w = synth.workloads()["llama8b_128k"]
+    for kw in w.runs:
+        _sampled(w, kw, pairs=[(0, 0), (0, 5)])
+
+
+def test_full_size_needles_1m():
+    w = synth.workloads()["needles_1m"]
+    for kw in w.runs:
+        _sampled(w, kw, pairs=[(0, 3)])
+
+
+def test_full_size_fold_256k():
+    w = synth.workloads()["fold_256k"]
+    for kw in (w.runs[0], w.runs[3], w.runs[5]):
+        _sampled(w, kw, pairs=[(0, 1)])
+
+
+def test_full_size_batch16_ragged():
+    w = synth.workloads()["batch16_ragged"]
+    for kw in w.runs:
+        _sampled(w, kw, pairs=[(0, 2), (7, 2), (15, 6)])
