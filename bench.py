@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Bench: draft-head decode attention over a very long paged KV cache, one MI355X.
+
+One step = one draft_attn_decode call: the device-side work decomposition, the
+split-K streaming pass over every visible K/V block and the log-sum-exp merge.
+Inputs (seeded, synthetic, bf16) are resident in HBM before timing starts.
+
+Default workload: the million-token draft step (1 sequence, 2^20 cached keys in
+16-token blocks behind a shuffled block table, 32 query / 8 kv heads, d = 128,
+8 draft tokens, 1% high-norm needle keys), full attention over the whole
+cache -- the read that grows with context. Printed: one JSON line with
+  value       KV GB/s of the whole step (algorithmic K+V bytes / wall time)
+  roofline    the streaming pass alone: algorithmic bytes / its mean duration
+              (HIP events recorded by the library around that launch), against
+              the 8 TB/s HBM peak; traffic = FETCH_SIZE + WRITE_SIZE bytes per
+              launch from rocprofv3 counters (profiles/traffic.json), when they
+              were taken on the current kernel source
+  cpu_baseline  the fp64 NumPy oracle on a bounded sample of the same step,
+              timed on this host's cores
+Options select other workloads and modes for sweeps; --gpus above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["draft_attention_amd/csrc/decode.hip", "draft_attention_amd/csrc/plan.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="needles_1m")
+    ap.add_argument("--run", type=int, default=0, help="index into the workload's mode list")
+    ap.add_argument("--split-keys", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def visible_keys(L, mode, window=0, n_sink=0, **_):
+    """Keys whose K and V a step must read (the visible set's size)."""
+    if mode == "window":
+        return min(L, n_sink + window)
+    return L
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime that torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def calib_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 3}), flush=True)
+
+
+def time_workload(w, kw, steps, warmup, seed, split, want_events=True):
+    """Generate inputs on the GPU, time `steps` decode calls; returns a result dict."""
+    import torch
+
+    import draft_attention_amd as da
+    import synth
+
+    dev = torch.device("cuda:0")
+    x = synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed, device=dev,
+                          fold=kw["mode"] == "fold", needle_frac=w.needle_frac, fill="zero")
+    side = x["k_side"] if kw["mode"] == "fold" else None
+    out = torch.empty((len(w.ctx_lens), w.T, w.Hq, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((len(w.ctx_lens), w.T, w.Hq), dtype=torch.float32, device=dev)
+    p = da.make_params(num_seqs=len(w.ctx_lens), num_draft_tokens=w.T, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
+                       head_dim=w.d, num_blocks=x["k_cache"].shape[0],
+                       max_blocks_per_seq=x["block_table"].shape[1], split_keys=split, rope_theta=w.rope_theta,
+                       **kw)
+    ws = torch.empty(da.workspace_size(p, w.ctx_lens), dtype=torch.uint8, device=dev)
+    _, chunk = da.plan(p, w.ctx_lens)
+    ev = HipEvents() if want_events else None
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)] if ev else [None] * steps
+
+    def step(pe):
+        da.decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], k_side=side,
+                  ctx_lens=w.ctx_lens, out=out, lse=lse, workspace=ws, rope_theta=w.rope_theta,
+                  split_keys=split, prof_events=pe, **kw)
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(pairs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    pass1 = None
+    if ev:
+        durs = [ev.elapsed_ms(a, b) for a, b in pairs]
+        pass1 = sum(durs) / len(durs)
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+    keys = sum(visible_keys(L, **kw) for L in w.ctx_lens) * w.Hkv
+    bytes_ = keys * 4 * w.d
+    res = dict(x=x, kw=kw, ms=ms, pass1_ms=pass1, bytes=bytes_, keys=keys // w.Hkv, chunk=chunk,
+               torch_ok=bool(torch.isfinite(out).all().item()))
+    return res
+
+
+def cpu_baseline(w, kw, x, budget_s):
+    """fp64 oracle on whole kv heads of the same step until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    G = w.Hq // w.Hkv
+    table = x["block_table"].cpu().numpy()
+    done_bytes, spent, heads = 0, 0.0, 0
+    for g in range(w.Hkv):
+        q = x["q"][:, :, g * G:(g + 1) * G].float().cpu().numpy()
+        k = x["k_cache"][:, g:g + 1].float().cpu().numpy()
+        v = x["v_cache"][:, g:g + 1].float().cpu().numpy()
+        ks = None if x["k_side"] is None else x["k_side"][:, g:g + 1].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, table, w.ctx_lens, k_side=ks, rope_theta=w.rope_theta, **kw)
+        spent += time.perf_counter() - t0
+        heads += 1
+        done_bytes += sum(visible_keys(L, **kw) for L in w.ctx_lens) * 4 * w.d
+        del q, k, v, ks
+        if spent >= budget_s:
+            break
+    return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{heads} of {w.Hkv} kv heads of the same step (all {sum(w.ctx_lens)} keys each), "
+                       f"fp64 NumPy, {spent:.1f} s")
+
+
+def traffic_for(tag):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(tag)
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path shards by sequence, kv head or key range, but no multi-GPU path is built).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+    import synth
+
+    wl = synth.workloads(args.seed)
+    w = wl[args.workload]
+    kw = w.runs[args.run]
+    r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys)
+    gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+    p1 = r["bytes"] / (r["pass1_ms"] * 1e-3) / 1e9
+    tag = f"{w.name}/{kw['mode']}"
+    secondary = {}
+    if not args.no_secondary and w.name == "needles_1m":
+        w2 = wl["llama8b_128k"]
+        r2 = time_workload(w2, w2.runs[0], args.steps, args.warmup, args.seed, 0, want_events=False)
+        secondary["llama8b_128k/full"] = dict(ms_per_step=round(r2["ms"], 5),
+                                              draft_steps_per_s=round(1e3 / r2["ms"], 1),
+                                              kv_gbs=round(r2["bytes"] / (r2["ms"] * 1e-3) / 1e9, 1))
+        del r2
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, kw, r["x"], args.cpu_budget_s)
+        cpu["value"] = round(cpu["value"], 4)
+    mode_str = kw["mode"] + ("" if kw["mode"] == "full" else f" W={kw.get('window', 0)} sinks={kw.get('n_sink', 0)}")
+    line = {
+        "metric": "draft-attention KV GB/s & % HBM peak; draft steps/s at 128K and 1M context",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": mode_str, "num_seqs": len(w.ctx_lens),
+                   "ctx_len": w.ctx_lens[0] if len(w.ctx_lens) == 1 else w.ctx_lens,
+                   "draft_tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "block_size": 16,
+                   "split_keys": r["chunk"], "alpha": kw.get("alpha", 1.0), "beta": kw.get("beta", 0.0),
+                   "kappa": kw.get("kappa", 0.0)},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "draft_steps_per_s": round(1e3 / r["ms"], 2),
+        "keys_per_s": round(r["keys"] / (r["ms"] * 1e-3), 1),
+        "kv_bytes_per_step": r["bytes"],
+        "roofline": {"bound": "hbm", "achieved": round(p1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(p1 / HBM_PEAK_GBS, 4), "traffic": traffic_for(tag),
+                     "kernel": "pass1_kernel (split-K K/V streaming)", "mean_launch_ms": round(r["pass1_ms"], 5)},
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+    }
+    if not r["torch_ok"]:
+        line["error"] = "non-finite output"
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,6 +61,12 @@ class DraftAttnError(RuntimeError):
 
 
 def _load():
+    # torch and this library must share one HIP runtime (both bind the soname
+    # libamdhip64.so.7): load torch's copy first when torch is installed.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "or python -m draft_attention_amd.build")

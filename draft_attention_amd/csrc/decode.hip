@@ -155,6 +155,13 @@ __device__ void seq_prefix(int32_t b, const int32_t* __restrict__ ctx_len, int32
 }
 
 // ---------------------------------------------------------------- pass 1
+// A work item (a chunk of C keys of one sequence, kv head and partition) is
+// streamed by a workgroup of kWaves waves; wave w takes the chunk's steps
+// w, w + kWaves, ..., so the four waves read neighbouring blocks at the same
+// time. Each wave keeps its own online-softmax state; at the end the states
+// are merged through LDS and the workgroup writes one record per query row.
+constexpr int kWaves = 4;
+
 template <int D>
 struct StepRegs {
   bf16x8 k[2][D / 32];  // A operands of the two S^T key tiles, per k-step
@@ -162,12 +169,21 @@ struct StepRegs {
   int32_t id0, id1;     // physical blocks of the step (-1: masked)
 };
 
+// Online-softmax state of one wave (log2 domain). l and l1 are lane-partial
+// over the four key groups until the end of streaming.
+template <int D, int RT>
+struct WaveState {
+  float m[RT], l[RT], l1[RT];
+  f32x4 o[RT][D / 16];
+};
+
 template <int D, int RT, bool FAR, bool LO>
-__device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* sbid, int32_t b, int32_t kvh,
-                                            int32_t kb, int32_t ke, int32_t part, int32_t w, float c2,
-                                            const bf16x8 (&qh)[RT][D / 32], const bf16x8 (&ql)[RT][D / 32]) {
+__device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* sbid, int32_t b, int32_t kvh,
+                                             int32_t kb, int32_t ke, int32_t part, float c2,
+                                             const bf16x8 (&qh)[RT][D / 32], const bf16x8 (&ql)[RT][D / 32],
+                                             WaveState<D, RT>& st) {
   constexpr int KS = D / 32, NT = D / 16;
-  const int lane = threadIdx.x, i16 = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, i16 = lane & 15, g = lane >> 4;
   const __bf16* __restrict__ kpool = FAR ? a.ks : a.k;
   const __bf16* __restrict__ vpool = a.v;
   const int32_t blk0 = kb >> 4;
@@ -181,17 +197,17 @@ __device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* s
   const bool sharp = FAR && (a.alpha != 1.f);
   const float alpha = a.alpha;
 
-  float m[RT], l[RT], l1[RT];
-  f32x4 o[RT][NT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
-    l[rt] = 0.f;
-    l1[rt] = 0.f;
+    st.m[rt] = -INFINITY;
+    st.l[rt] = 0.f;
+    st.l1[rt] = 0.f;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) st.o[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // K/V are read once per call: nontemporal loads keep them from displacing
+  // anything in the caches.
   auto issue = [&](int32_t s, StepRegs<D>& r) {
     r.id0 = sbid[2 * s];
     r.id1 = sbid[2 * s + 1];
@@ -204,9 +220,10 @@ __device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* s
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) r.k[t][ks] = *(const bf16x8*)(kp + t * 4 * D + ks * 32);
+      for (int ks = 0; ks < KS; ++ks)
+        r.k[t][ks] = __builtin_nontemporal_load((const bf16x8*)(kp + t * 4 * D + ks * 32));
 #pragma unroll
-    for (int n = 0; n < NT; ++n) r.v[n] = *(const bf16x8*)(vp + n * 256);
+    for (int n = 0; n < NT; ++n) r.v[n] = __builtin_nontemporal_load((const bf16x8*)(vp + n * 256));
   };
 
   auto compute = [&](int32_t s, StepRegs<D>& r) {
@@ -258,13 +275,13 @@ __device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* s
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
       mx = pair_max32(pair_max16(mx));
-      const float mnew = fmaxf(m[rt], mx);
+      const float mnew = fmaxf(st.m[rt], mx);
       const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float corr = ex2(m[rt] - mref);
+      const float corr = ex2(st.m[rt] - mref);
       bf16x8 pb;
       float psum = 0.f;
       if (sharp) {
-        const float corr_a = ex2(alpha * (m[rt] - mref));
+        const float corr_a = ex2(alpha * (st.m[rt] - mref));
         float pasum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -275,10 +292,10 @@ __device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* s
           pasum += pa;
           pb[e] = (__bf16)pa;
         }
-        l1[rt] = l1[rt] * corr + psum;
-        l[rt] = l[rt] * corr_a + pasum;
+        st.l1[rt] = st.l1[rt] * corr + psum;
+        st.l[rt] = st.l[rt] * corr_a + pasum;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) o[rt][n] *= corr_a;
+        for (int n = 0; n < NT; ++n) st.o[rt][n] *= corr_a;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -286,55 +303,63 @@ __device__ __forceinline__ void stream_item(const Pass1Args& a, const int32_t* s
           psum += p;
           pb[e] = (__bf16)p;
         }
-        l[rt] = l[rt] * corr + psum;
+        st.l[rt] = st.l[rt] * corr + psum;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) o[rt][n] *= corr;
+        for (int n = 0; n < NT; ++n) st.o[rt][n] *= corr;
       }
-      m[rt] = mnew;
+      st.m[rt] = mnew;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[n], pb, o[rt][n], 0, 0, 0);
+      for (int n = 0; n < NT; ++n)
+        st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[n], pb, st.o[rt][n], 0, 0, 0);
     }
   };
 
-  StepRegs<D> ra, rb;
-  issue(0, ra);
-  int32_t s = 0;
-  for (;;) {
-    if (s + 1 < nsteps) issue(s + 1, rb);
-    compute(s, ra);
-    if (++s >= nsteps) break;
-    if (s + 1 < nsteps) issue(s + 1, ra);
-    compute(s, rb);
-    if (++s >= nsteps) break;
+  int32_t s = wave;
+  if (s < nsteps) {
+    StepRegs<D> ra, rb;
+    issue(s, ra);
+    for (;;) {
+      if (s + kWaves < nsteps) issue(s + kWaves, rb);
+      compute(s, ra);
+      s += kWaves;
+      if (s >= nsteps) break;
+      if (s + kWaves < nsteps) issue(s + kWaves, ra);
+      compute(s, rb);
+      s += kWaves;
+      if (s >= nsteps) break;
+    }
   }
-
-  // Row sums are lane-partial over the four key groups: reduce, then write.
-  const size_t rowbase = (size_t)w * a.rows_pad;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float lsum = pair_add32(pair_add16(l[rt]));
-    const float l1sum = sharp ? pair_add32(pair_add16(l1[rt])) : lsum;
-    const int32_t row = 16 * rt + i16;
-    if (row < a.R) {
-      float* dst = a.acc + (rowbase + row) * D + 4 * g;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) *(f32x4*)(dst + 16 * n) = o[rt][n];
-      if (g == 0) a.stat[rowbase + row] = make_float4(m[rt], lsum, l1sum, 0.f);
-    }
+    st.l[rt] = pair_add32(pair_add16(st.l[rt]));
+    st.l1[rt] = sharp ? pair_add32(pair_add16(st.l1[rt])) : st.l[rt];
   }
 }
 
+// Dynamic LDS of pass 1: block ids of the chunk, then the merge buffers.
+__host__ __device__ inline size_t pass1_sbid_bytes(int32_t C) { return ((size_t)(C / 16 + 2) * 4 + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t pass1_lds_bytes(int32_t C, int32_t rows_pad, int32_t D) {
+  return pass1_sbid_bytes(C) + (size_t)kWaves * rows_pad * (sizeof(float) + sizeof(float2)) +
+         (size_t)2 * rows_pad * (D + 4) * sizeof(float);
+}
+
 template <int D, int RT, bool FOLDK>
-__global__ __launch_bounds__(64) void pass1_kernel(const Pass1Args a) {
-  constexpr int KS = D / 32;
-  extern __shared__ int32_t sbid[];
-  const int lane = threadIdx.x, i16 = lane & 15, g = lane >> 4;
+__global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
+  constexpr int KS = D / 32, NT = D / 16, OS = D + 4;  // OS: padded LDS row stride (floats)
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i16 = lane & 15, g = lane >> 4;
   const int32_t w = blockIdx.x;
+  const int32_t rp = a.rows_pad;
+  int32_t* sbid = (int32_t*)smem;
+  float* s_m = (float*)(smem + pass1_sbid_bytes(a.C));  // [kWaves][rp] row maxima
+  float2* s_l = (float2*)(s_m + kWaves * rp);           // [kWaves][rp] (acc denominator, plain sum)
+  float* s_o = (float*)(s_l + kWaves * rp);              // [2][rp][OS] partial outputs
   SeqInfo si;
   if (!locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si)) {
     // Only when ctx_len on the device disagrees with the host mirror: leave a
     // neutral record so the merge stays defined.
-    if (lane < a.R) a.stat[(size_t)w * a.rows_pad + lane] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    if (tid < a.R) a.stat[(size_t)w * rp + tid] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    for (int32_t i = tid; i < a.R * D; i += 256) a.acc[(size_t)w * rp * D + i] = 0.f;
     return;
   }
   const int32_t b = si.b;
@@ -349,7 +374,7 @@ __global__ __launch_bounds__(64) void pass1_kernel(const Pass1Args a) {
   const int32_t blk0 = kb >> 4;
   const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  for (int32_t j = lane; j < nblk + 1; j += 64) {
+  for (int32_t j = tid; j < nblk + 1; j += 256) {
     int32_t id = -1;
     if (j < nblk && blk0 + j < a.max_blocks) {
       id = trow[blk0 + j];
@@ -383,7 +408,9 @@ __global__ __launch_bounds__(64) void pass1_kernel(const Pass1Args a) {
     }
   }
 
-  if (FOLDK && part == kPartFar) {
+  WaveState<D, RT> st;
+  const bool far_part = FOLDK && part == kPartFar;
+  if (far_part) {
     if (a.rope == DRAFT_ATTN_ROPE_NEOX) {
       // Far query q_far = R(-P_v) q, P_v = L - W - 1 [FOLD]. Lane (i16, g) holds
       // channels 32ks + 8g + e; the rotation partner d/2 away sits in k-step
@@ -415,25 +442,88 @@ __global__ __launch_bounds__(64) void pass1_kernel(const Pass1Args a) {
             ql[rt][ks + KS / 2][e] = (__bf16)(y2 - (float)h2);
           }
         }
-      stream_item<D, RT, true, true>(a, sbid, b, kvh, kb, ke, part, w, c2, qh, ql);
+      stream_steps<D, RT, true, true>(a, sbid, b, kvh, kb, ke, part, c2, qh, ql, st);
     } else {
-      stream_item<D, RT, true, false>(a, sbid, b, kvh, kb, ke, part, w, c2, qh, ql);
+      stream_steps<D, RT, true, false>(a, sbid, b, kvh, kb, ke, part, c2, qh, ql, st);
     }
   } else {
-    stream_item<D, RT, false, false>(a, sbid, b, kvh, kb, ke, part, w, c2, qh, ql);
+    stream_steps<D, RT, false, false>(a, sbid, b, kvh, kb, ke, part, c2, qh, ql, st);
+  }
+
+  // ---- merge the waves: common row maxima, rescale, sum through two LDS slots.
+  if (g == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) s_m[wave * rp + 16 * rt + i16] = st.m[rt];
+  }
+  __syncthreads();
+  const bool sharp = far_part && (a.alpha != 1.f);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * rt + i16;
+    float M = s_m[row];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, s_m[k * rp + row]);
+    const float d0 = M == -INFINITY ? -INFINITY : st.m[rt] - M;
+    const float f = ex2(d0);
+    const float fa = sharp ? ex2(a.alpha * d0) : f;
+#pragma unroll
+    for (int n2 = 0; n2 < NT; ++n2) st.o[rt][n2] *= fa;
+    if (g == 0) s_l[wave * rp + row] = make_float2(st.l[rt] * fa, st.l1[rt] * f);
+  }
+  if (wave >= 2) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int n2 = 0; n2 < NT; ++n2)
+        *(f32x4*)(s_o + ((wave - 2) * rp + 16 * rt + i16) * OS + 16 * n2 + 4 * g) = st.o[rt][n2];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int n2 = 0; n2 < NT; ++n2) {
+        f32x4* p = (f32x4*)(s_o + (wave * rp + 16 * rt + i16) * OS + 16 * n2 + 4 * g);
+        *p = *p + st.o[rt][n2];
+      }
+  }
+  __syncthreads();
+  const size_t rowbase = (size_t)w * rp;
+  for (int32_t idx = tid; idx < a.R * (D / 4); idx += 256) {
+    const int32_t row = idx / (D / 4), q4 = idx - row * (D / 4);
+    const f32x4 v0 = *(const f32x4*)(s_o + row * OS + 4 * q4);
+    const f32x4 v1 = *(const f32x4*)(s_o + (rp + row) * OS + 4 * q4);
+    *(f32x4*)(a.acc + (rowbase + row) * D + 4 * q4) = v0 + v1;
+  }
+  if (tid < a.R) {
+    float M = s_m[tid], Lsum = 0.f, L1sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      M = fmaxf(M, s_m[k * rp + tid]);
+      Lsum += s_l[k * rp + tid].x;
+      L1sum += s_l[k * rp + tid].y;
+    }
+    a.stat[rowbase + tid] = make_float4(M, Lsum, L1sum, 0.f);
   }
 }
 
 // ---------------------------------------------------------------- pass 2
-// One workgroup of four waves per output row (sequence, kv head, query row):
-// the waves split the row's work items, keep running log-sum-exp records, and
-// wave 0 merges the four records and, for FOLD, the two partitions.
+// One workgroup of 256 threads per output row (sequence, kv head, query row).
+// Phase 1 reduces the row's item records to partition maxima and sums; phase 2
+// gathers the unnormalised partial outputs, thread (group g, channel quad c)
+// summing items g, g + NG, ... with per-item scales staged in LDS, so every
+// load of a phase is independent and many are in flight at once. FOLD's
+// partitions are then combined with beta.
 template <int D>
 __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
-  constexpr int CPL = D / 64;  // channels per lane
-  __shared__ float red_main[4][D + 2];
-  __shared__ float red_far[4][D + 3];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int NQ = D / 4;     // float4 channel quads per row
+  constexpr int NG = 256 / NQ;  // item groups
+  constexpr int TILE = 1024;    // items whose scales are staged at once
+  __shared__ float s_scale[TILE];
+  __shared__ float4 s_part[2][NG][NQ];
+  __shared__ float s_red[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q4 = tid % NQ, grp = tid / NQ;
   const int32_t idx = blockIdx.x;
   const int32_t row = idx % a.R;
   const int32_t bh = idx / a.R;
@@ -448,122 +538,114 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   i0 = i0 < lim ? i0 : lim;
   im = im < lim ? im : lim;
   i1 = i1 < lim ? i1 : lim;
-
-  float M = -INFINITY, Ls = 0.f, acc[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-  for (int64_t it = i0 + wv; it < im; it += 4) {
-    const size_t r = (size_t)it * a.rows_pad + row;
-    const float4 st = a.stat[r];
-    const float* src = a.acc + r * D + lane * CPL;
-    float v[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = src[c];
-    if (st.x == -INFINITY) continue;
-    const float Mn = fmaxf(M, st.x);
-    const float so = exp2f(M - Mn), si_ = exp2f(st.x - Mn);
-    Ls = Ls * so + st.y * si_;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * so + v[c] * si_;
-    M = Mn;
-  }
-  float MF = -INFINITY, ZF = 0.f, ZFa = 0.f, accF[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) accF[c] = 0.f;
   const float alpha = a.alpha;
-  for (int64_t it = im + wv; it < i1; it += 4) {
-    const size_t r = (size_t)it * a.rows_pad + row;
-    const float4 st = a.stat[r];
-    const float* src = a.acc + r * D + lane * CPL;
-    float v[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = src[c];
-    if (st.x == -INFINITY) continue;
-    const float Mn = fmaxf(MF, st.x);
-    const float so = exp2f(MF - Mn), si_ = exp2f(st.x - Mn);
-    const float soa = exp2f(alpha * (MF - Mn)), sia = exp2f(alpha * (st.x - Mn));
-    ZF = ZF * so + st.z * si_;
-    ZFa = ZFa * soa + st.y * sia;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) accF[c] = accF[c] * soa + v[c] * sia;
-    MF = Mn;
+  const size_t rp = (size_t)a.rows_pad;
+
+  // Phase 1a: maxima of the two partitions.
+  float mM = -INFINITY, mF = -INFINITY;
+  for (int64_t i = i0 + tid; i < i1; i += 256) {
+    const float m = a.stat[(size_t)i * rp + row].x;
+    if (i < im) mM = fmaxf(mM, m);
+    else mF = fmaxf(mF, m);
   }
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    red_main[wv][2 + lane * CPL + c] = acc[c];
-    red_far[wv][3 + lane * CPL + c] = accF[c];
+  for (int off = 32; off >= 1; off >>= 1) {
+    mM = fmaxf(mM, __shfl_xor(mM, off, 64));
+    mF = fmaxf(mF, __shfl_xor(mF, off, 64));
   }
-  if (lane == 0) {
-    red_main[wv][0] = M;
-    red_main[wv][1] = Ls;
-    red_far[wv][0] = MF;
-    red_far[wv][1] = ZF;
-    red_far[wv][2] = ZFa;
-  }
+  if (lane == 0) { s_red[wv][0] = mM; s_red[wv][1] = mF; }
   __syncthreads();
-  if (wv != 0) return;
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
+  const float MF = fmaxf(fmaxf(s_red[0][1], s_red[1][1]), fmaxf(s_red[2][1], s_red[3][1]));
+  __syncthreads();
 
-  M = -INFINITY;
-  Ls = 0.f;
-  MF = -INFINITY;
-  ZF = 0.f;
-  ZFa = 0.f;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = accF[c] = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float mk = red_main[k][0];
-    if (mk != -INFINITY) {
-      const float Mn = fmaxf(M, mk);
-      const float so = exp2f(M - Mn), si_ = exp2f(mk - Mn);
-      Ls = Ls * so + red_main[k][1] * si_;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = acc[c] * so + red_main[k][2 + lane * CPL + c] * si_;
-      M = Mn;
-    }
-    const float mf = red_far[k][0];
-    if (mf != -INFINITY) {
-      const float Mn = fmaxf(MF, mf);
-      const float so = exp2f(MF - Mn), si_ = exp2f(mf - Mn);
-      const float soa = exp2f(alpha * (MF - Mn)), sia = exp2f(alpha * (mf - Mn));
-      ZF = ZF * so + red_far[k][1] * si_;
-      ZFa = ZFa * soa + red_far[k][2] * sia;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) accF[c] = accF[c] * soa + red_far[k][3 + lane * CPL + c] * sia;
-      MF = Mn;
+  // Phase 1b: partition sums rescaled to the maxima.
+  float Ls = 0.f, ZF = 0.f, ZFa = 0.f;
+  for (int64_t i = i0 + tid; i < i1; i += 256) {
+    const float4 st = a.stat[(size_t)i * rp + row];
+    if (st.x == -INFINITY) continue;
+    if (i < im) {
+      Ls += st.y * exp2f(st.x - M);
+    } else {
+      ZF += st.z * exp2f(st.x - MF);
+      ZFa += st.y * exp2f(alpha * (st.x - MF));
     }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Ls += __shfl_xor(Ls, off, 64);
+    ZF += __shfl_xor(ZF, off, 64);
+    ZFa += __shfl_xor(ZFa, off, 64);
+  }
+  if (lane == 0) { s_red[wv][0] = Ls; s_red[wv][1] = ZF; s_red[wv][2] = ZFa; }
+  __syncthreads();
+  Ls = s_red[0][0] + s_red[1][0] + s_red[2][0] + s_red[3][0];
+  ZF = s_red[0][1] + s_red[1][1] + s_red[2][1] + s_red[3][1];
+  ZFa = s_red[0][2] + s_red[1][2] + s_red[2][2] + s_red[3][2];
 
-  // log2 weights of the partitions; FOLD weighs the far memory by e^beta Z_F.
+  // Phase 2: scaled sums of the partial outputs, main items then far items.
+  float4 accp[2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t lo = pt == 0 ? i0 : im, hi = pt == 0 ? im : i1;
+    const float ref = pt == 0 ? M : MF;
+    const float sh = pt == 0 ? 1.f : alpha;
+    for (int64_t t0 = lo; t0 < hi; t0 += TILE) {
+      const int64_t t1 = hi < t0 + TILE ? hi : t0 + TILE;
+      __syncthreads();
+      for (int64_t i = t0 + tid; i < t1; i += 256) {
+        const float m = a.stat[(size_t)i * rp + row].x;
+        s_scale[i - t0] = m == -INFINITY ? 0.f : exp2f(sh * (m - ref));
+      }
+      __syncthreads();
+      const float* base = a.acc + row * (size_t)D + 4 * q4;
+#pragma unroll 8
+      for (int64_t i = t0 + grp; i < t1; i += NG) {
+        const float4 v = *(const float4*)(base + (size_t)i * rp * D);
+        const float sc = s_scale[i - t0];
+        acc.x += sc * v.x;
+        acc.y += sc * v.y;
+        acc.z += sc * v.z;
+        acc.w += sc * v.w;
+      }
+    }
+    accp[pt] = acc;
+  }
+  s_part[0][grp][q4] = accp[0];
+  s_part[1][grp][q4] = accp[1];
+  __syncthreads();
+
+  // Final combine: thread c < D owns output channel c.
   const float lwL = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
   const float lwF = ZF > 0.f ? a.beta * kLog2e + MF + log2f(ZF) : -INFINITY;
   const float top = fmaxf(lwL, lwF);
-  float res[CPL];
-  float lse_out;
-  if (top == -INFINITY) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) res[c] = 0.f;
-    lse_out = -INFINITY;
-  } else {
-    const float wL = exp2f(lwL - top), wF = exp2f(lwF - top);
-    const float den = wL + wF;
-    const float fl = wL > 0.f ? wL / (den * Ls) : 0.f;
-    const float ff = wF > 0.f ? wF / (den * ZFa) : 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) res[c] = acc[c] * fl + accF[c] * ff;
-    lse_out = (top + log2f(den)) * kLn2;
-  }
   const int32_t t = row / a.G;
   const int32_t head = kvh * a.G + (row - t * a.G);
   const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
-  float* dst = a.out + orow * D + lane * CPL;
-  if (CPL == 2) {
-    *(float2*)dst = make_float2(res[0], res[CPL - 1]);
-  } else {
+  if (tid < D) {
+    const float* pm = (const float*)&s_part[0][0][0];
+    const float* pf = (const float*)&s_part[1][0][0];
+    float sm = 0.f, sf = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) dst[c] = res[c];
+    for (int g2 = 0; g2 < NG; ++g2) {
+      sm += pm[g2 * D + tid];
+      sf += pf[g2 * D + tid];
+    }
+    float res = 0.f;
+    if (top != -INFINITY) {
+      const float wL = exp2f(lwL - top), wF = exp2f(lwF - top);
+      const float den = wL + wF;
+      const float fl = wL > 0.f ? wL / (den * Ls) : 0.f;
+      const float ff = wF > 0.f ? wF / (den * ZFa) : 0.f;
+      res = sm * fl + sf * ff;
+    }
+    a.out[orow * D + tid] = res;
   }
-  if (lane == 0) a.lse[orow] = lse_out;
+  if (tid == 0) {
+    const float den = exp2f(lwL - top) + exp2f(lwF - top);
+    a.lse[orow] = top == -INFINITY ? -INFINITY : (top + log2f(den)) * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------- launch
@@ -571,11 +653,11 @@ template <int D>
 static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t grid, size_t lds,
                          hipStream_t s) {
   if (row_tiles == 1) {
-    if (fold) pass1_kernel<D, 1, true><<<grid, 64, lds, s>>>(a);
-    else pass1_kernel<D, 1, false><<<grid, 64, lds, s>>>(a);
+    if (fold) pass1_kernel<D, 1, true><<<grid, 64 * kWaves, lds, s>>>(a);
+    else pass1_kernel<D, 1, false><<<grid, 64 * kWaves, lds, s>>>(a);
   } else {
-    if (fold) pass1_kernel<D, 2, true><<<grid, 64, lds, s>>>(a);
-    else pass1_kernel<D, 2, false><<<grid, 64, lds, s>>>(a);
+    if (fold) pass1_kernel<D, 2, true><<<grid, 64 * kWaves, lds, s>>>(a);
+    else pass1_kernel<D, 2, false><<<grid, 64 * kWaves, lds, s>>>(a);
   }
 }
 
@@ -660,7 +742,7 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   (void)hipGetLastError();  // clear a stale error so the check below reports ours
   if (p->prof_events[0]) (void)hipEventRecord((hipEvent_t)p->prof_events[0], s);
   if (pr.total_items > 0) {
-    const size_t lds = (size_t)(pr.chunk / 16 + 2) * sizeof(int32_t);
+    const size_t lds = pass1_lds_bytes(pr.chunk, pr.rows_pad, D);
     const bool fold = p->mode == kFold;
     if (D == 64) launch_pass1<64>(a1, pr.row_tiles, fold, (uint32_t)pr.total_items, lds, s);
     else launch_pass1<128>(a1, pr.row_tiles, fold, (uint32_t)pr.total_items, lds, s);

@@ -11,11 +11,13 @@ namespace da {
 
 namespace {
 
-// Aim for this many work items: a few per wave slot, so the split-K grid
-// fills the 256 compute units and finishes evenly.
-constexpr int64_t kTargetItems = 2048;
-constexpr int32_t kMinAutoChunk = 256;
-constexpr int32_t kMaxAutoChunk = 8192;
+// Aim for this many work items. Each item is streamed by one 4-wave
+// workgroup, and one such workgroup per compute unit is resident, so 512 items
+// are two rounds over the 256 compute units. The smallest chunk gives every
+// wave one 32-key step; long contexts stop growing the chunk at 32768 keys.
+constexpr int64_t kTargetItems = 512;
+constexpr int32_t kMinAutoChunk = 128;
+constexpr int32_t kMaxAutoChunk = 32768;
 constexpr int32_t kMaxChunk = 65536;
 constexpr int32_t kMaxLen = 1 << 30;
 

@@ -200,11 +200,11 @@ def test_auto_chunk_size_targets_the_workloads():
     p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="full",
                max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
     items, C = da().plan(p, [1 << 20])
-    assert C == 4096 and len(items) == 2048
+    assert C == 16384 and len(items) == 512
     p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=4, mode="full",
                max_blocks_per_seq=1 << 13, num_blocks=1 << 14)
     items, C = da().plan(p, [131072])
-    assert C == 512 and len(items) == 2048
+    assert C == 2048 and len(items) == 512
 
 
 def test_host_logic_under_sanitizers(tmp_path):
