@@ -13,10 +13,10 @@
 //
 // Design. The call is bound by HBM: every visible key costs 4*d bytes of K and V
 // read once. Pass 1 splits the key axis of every (sequence, kv head) into work
-// items of C keys (plan.h); one 64-lane wave streams an item in steps of two
-// 16-token blocks (32 keys), keeping the whole GQA group x draft-token row set
-// (R <= 32 rows) of its kv head in registers, so each K/V byte is loaded by
-// exactly one wave:
+// items of C keys (plan.h). A 256-thread workgroup streams one item; its four
+// waves take interleaved steps of two 16-token blocks (32 keys) and each keeps
+// the whole GQA group x draft-token row set (R <= 32 rows) of its kv head in
+// registers, so each K/V byte is loaded exactly once:
 //   S^T[key][row] = K . Q^T   on v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q rows)
 //   online softmax per row    in the MFMA output layout: lane (row = l%16) holds
 //                             keys 4*(l/16)+r, so row statistics reduce with two
@@ -24,10 +24,11 @@
 //   O^T[chan][row] += V^T . P^T  on the same MFMA: A = V^T comes straight from the
 //                             channel-major value block (one 16-byte load = 8
 //                             consecutive keys of one channel), B = P in bf16.
-// K and V fragments go from HBM to registers with 128-bit loads and no LDS
-// staging; the next step's loads are issued before the current step computes.
-// The key permutation inside a step is chosen so that the softmax output of the
-// Q.K^T product is already the B operand of the P.V product.
+// K and V fragments go from HBM to registers with 128-bit nontemporal loads and
+// no LDS staging; the next step's loads are issued before the current step
+// computes. The key permutation inside a step is chosen so that the softmax
+// output of the Q.K^T product is already the B operand of the P.V product. The
+// four waves' states merge through LDS into one record per item and row.
 // Pass 2 merges the per-item (max, sums, unnormalised output) records with the
 // log-sum-exp rule, then combines FOLD's local and far partitions with beta.
 #include <hip/hip_runtime.h>
