@@ -11,15 +11,66 @@ namespace da {
 
 namespace {
 
-// Aim for this many work items. Each item is streamed by one 4-wave
-// workgroup, and one such workgroup per compute unit is resident, so 512 items
-// are two rounds over the 256 compute units. The smallest chunk gives every
-// wave one 32-key step; long contexts stop growing the chunk at 32768 keys.
-constexpr int64_t kTargetItems = 512;
-constexpr int32_t kMinAutoChunk = 128;
-constexpr int32_t kMaxAutoChunk = 32768;
-constexpr int32_t kMaxChunk = 65536;
+// Chunk-size model. Each work item is streamed by one 4-wave workgroup; the
+// number resident per compute unit is register-limited (compiler resource
+// usage for gfx950: head_dim 128 -> 1; head_dim 64 -> 3 with one row tile, 2
+// with two). With near-equal chunks of at most P keys, r rounds over the
+// resident slots take about r * (P + kItemOverheadKeys) key-steps, the
+// overhead being an item's start-up (block-table and query loads before the
+// first K/V load). The planner tries 1..kMaxRounds rounds and keeps the
+// cheapest.
+constexpr int32_t kComputeUnits = 256;  // MI355X
+constexpr int64_t kItemOverheadKeys = 256;
+constexpr int32_t kMaxRounds = 4;
+constexpr int32_t kMinAutoChunk = 128;  // one 32-key step per wave
+constexpr int32_t kMaxChunk = 65536;    // bounds the block-id table kept in LDS
 constexpr int32_t kMaxLen = 1 << 30;
+
+int32_t resident_per_cu(int32_t D, int32_t row_tiles) { return D == 128 ? 1 : (row_tiles == 1 ? 3 : 2); }
+
+int32_t round_up_32(int64_t x) { return (int32_t)((x + 31) / 32 * 32); }
+
+int64_t count_items(const draft_attn_params* p, const int32_t* lens, int32_t P) {
+  int64_t items = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b)
+    items += (int64_t)seq_items(seq_ranges(lens[b], p->mode, p->window, p->n_sink), P, nullptr) * p->num_kv_heads;
+  return items;
+}
+
+// Smallest P in [lo, kMaxChunk] (multiple of 32) with at most `budget` items;
+// kMaxChunk when none fits. Item count does not grow with P.
+int32_t fit_chunk(const draft_attn_params* p, const int32_t* lens, int32_t lo, int64_t budget) {
+  if (count_items(p, lens, lo) <= budget) return lo;
+  int32_t bad = lo, good = kMaxChunk;
+  if (count_items(p, lens, good) > budget) return good;
+  while (good - bad > 32) {
+    const int32_t mid = round_up_32(((int64_t)bad + good) / 2);
+    if (mid >= good) break;
+    if (count_items(p, lens, mid) <= budget) good = mid;
+    else bad = mid;
+  }
+  return good;
+}
+
+int32_t choose_chunk(const draft_attn_params* p, const int32_t* lens, int64_t keyheads, int32_t row_tiles) {
+  const int64_t slots = (int64_t)kComputeUnits * resident_per_cu(p->head_dim, row_tiles);
+  int32_t best = kMinAutoChunk;
+  int64_t best_cost = -1;
+  for (int32_t r = 1; r <= kMaxRounds; ++r) {
+    const int64_t budget = r * slots;
+    int64_t lo = (keyheads + budget - 1) / budget;
+    lo = lo < kMinAutoChunk ? kMinAutoChunk : (lo > kMaxChunk ? kMaxChunk : lo);
+    const int32_t P = fit_chunk(p, lens, round_up_32(lo), budget);
+    const int64_t items = count_items(p, lens, P);
+    const int64_t rounds = (items + slots - 1) / slots;
+    const int64_t cost = (rounds > 0 ? rounds : 1) * ((int64_t)P + kItemOverheadKeys);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = P;
+    }
+  }
+  return best;
+}
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -73,18 +124,9 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   const int64_t R = (int64_t)G * T;
   if (R > DRAFT_ATTN_MAX_ROWS) return DRAFT_ATTN_ENOTSUP;
 
-  int32_t C = p->split_keys;
-  if (C == 0) {
-    const int64_t want = (keyheads + kTargetItems - 1) / kTargetItems;
-    C = kMinAutoChunk;
-    while (C < kMaxAutoChunk && C < want) C *= 2;
-  }
-
-  int64_t items = 0;
-  for (int32_t b = 0; b < B; ++b) {
-    const Ranges r = seq_ranges(ctx_len_host[b], p->mode, p->window, p->n_sink);
-    items += (int64_t)seq_items(r, C, nullptr) * Hkv;
-  }
+  const int32_t row_tiles = (int32_t)((R + 15) / 16);
+  const int32_t C = p->split_keys != 0 ? p->split_keys : choose_chunk(p, ctx_len_host, keyheads, row_tiles);
+  const int64_t items = count_items(p, ctx_len_host, C);
   if (items > 0x7fffffff) return DRAFT_ATTN_EINVAL;
   if ((int64_t)B * Hkv * R > 0x7fffffff) return DRAFT_ATTN_EINVAL;
 
@@ -92,7 +134,7 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   out->total_items = items;
   out->G = G;
   out->rows = (int32_t)R;
-  out->row_tiles = (int32_t)((R + 15) / 16);
+  out->row_tiles = row_tiles;
   out->rows_pad = 16 * out->row_tiles;
   const size_t nrows = (size_t)items * (size_t)out->rows_pad;
   out->stat_offset = 0;

@@ -4,9 +4,11 @@
 // "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
 // Context", Abstract, and the local/far split of "FOLD: Position-Free Far
 // Memory with Local Order for Long-Context Speculative Decoding", summary).
-// Each range is cut at multiples of the chunk size C (a multiple of 32 keys),
-// so a chunk never straddles a range or partition boundary. Work items are
-// ordered sequence-major, then kv head, then range, then chunk; the ranges of
+// Given a target chunk size P (a multiple of 32 keys), a range of len keys is
+// cut into ceil(len / P) near-equal chunks of round_up_32(ceil(len / np)) keys,
+// counted from the range's first key, so a chunk never straddles a range or
+// partition boundary and no chunk exceeds P keys. Work items are ordered
+// sequence-major, then kv head, then range, then chunk; the ranges of
 // partition 0 (keys from k_cache) come before partition 1 (FOLD far keys from
 // k_side). The kernels recompute this decomposition from ctx_len on the device
 // instead of reading a work list, so nothing is copied from the host per call.
@@ -61,15 +63,25 @@ DA_HD Ranges seq_ranges(int32_t L, int32_t mode, int32_t W, int32_t S) {
   return make_ranges(1, 0, ws, kPartFar, 0, 0, kPartMain);
 }
 
-// Number of C-aligned chunks covering [a, e).
-DA_HD int32_t range_chunks(int32_t a, int32_t e, int32_t C) {
-  return e > a ? (e - 1) / C - a / C + 1 : 0;
+// Chunk length for a range of len > 0 keys under target P: np = ceil(len / P)
+// near-equal chunks, rounded up to whole 32-key steps (never above P).
+DA_HD int32_t range_chunk_len(int32_t len, int32_t P) {
+  const int32_t np = (len + P - 1) / P;
+  const int32_t c = (len + np - 1) / np;
+  return (c + 31) & ~31;
+}
+
+// Number of chunks covering [a, e).
+DA_HD int32_t range_chunks(int32_t a, int32_t e, int32_t P) {
+  if (e <= a) return 0;
+  const int32_t len = e - a, c = range_chunk_len(len, P);
+  return (len + c - 1) / c;
 }
 
 // Work items of one (sequence, kv head); *n_main receives those of partition 0.
-DA_HD int32_t seq_items(const Ranges& r, int32_t C, int32_t* n_main) {
-  const int32_t c0 = r.n > 0 ? range_chunks(r.a0, r.e0, C) : 0;
-  const int32_t c1 = r.n > 1 ? range_chunks(r.a1, r.e1, C) : 0;
+DA_HD int32_t seq_items(const Ranges& r, int32_t P, int32_t* n_main) {
+  const int32_t c0 = r.n > 0 ? range_chunks(r.a0, r.e0, P) : 0;
+  const int32_t c1 = r.n > 1 ? range_chunks(r.a1, r.e1, P) : 0;
   if (n_main) *n_main = (r.p0 == kPartMain ? c0 : 0) + (r.p1 == kPartMain ? c1 : 0);
   return c0 + c1;
 }
@@ -87,16 +99,16 @@ DA_HD int32_t visible_count(int32_t L, int32_t mode, int32_t W, int32_t S) {
 }
 
 // Bounds of item k (0 <= k < seq_items) of a (sequence, kv head).
-DA_HD void item_bounds(const Ranges& r, int32_t k, int32_t C, int32_t* kb, int32_t* ke,
+DA_HD void item_bounds(const Ranges& r, int32_t k, int32_t P, int32_t* kb, int32_t* ke,
                        int32_t* part) {
-  const int32_t c0 = r.n > 0 ? range_chunks(r.a0, r.e0, C) : 0;
+  const int32_t c0 = r.n > 0 ? range_chunks(r.a0, r.e0, P) : 0;
   const bool first = k < c0;
   const int32_t a = first ? r.a0 : r.a1;
   const int32_t e = first ? r.e0 : r.e1;
   const int32_t kk = first ? k : k - c0;
-  const int32_t ch = a / C + kk;
-  *kb = imax(a, ch * C);
-  *ke = imin(e, (ch + 1) * C);
+  const int32_t c = range_chunk_len(e - a, P);
+  *kb = a + kk * c;
+  *ke = imin(e, *kb + c);
   *part = first ? r.p0 : r.p1;
 }
 

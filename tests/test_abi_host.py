@@ -168,8 +168,7 @@ def _check_plan(mode, W, S, lens, Hkv, split):
     prev = (-1, -1, -1)
     for (b, h, kb, ke, part) in items:
         assert 0 <= b < len(lens) and 0 <= h < Hkv and kb < ke and part in (0, 1)
-        assert kb // C == (ke - 1) // C, "chunk straddles a C boundary"
-        key = (b, h)
+        assert ke - kb <= C, "chunk longer than the target"
         assert (b, h, part) >= prev, "launch order is sequence, kv head, partition"
         prev = (b, h, part)
         seen.setdefault((b, h, part), []).append((kb, ke))
@@ -196,15 +195,37 @@ def test_plan_covers_the_oracle_index_sets():
         _check_plan(mode, W, S, lens, rnd.choice([1, 2, 8]), split)
 
 
-def test_auto_chunk_size_targets_the_workloads():
+def test_auto_chunk_size_balances_the_workloads():
+    # One sequence of 2^20 keys, 8 kv heads: 256 equal chunks (one per compute unit).
     p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="full",
                max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
     items, C = da().plan(p, [1 << 20])
-    assert C == 16384 and len(items) == 512
-    p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=4, mode="full",
-               max_blocks_per_seq=1 << 13, num_blocks=1 << 14)
-    items, C = da().plan(p, [131072])
-    assert C == 2048 and len(items) == 512
+    assert C == 32768 and len(items) == 256 and {ke - kb for (_, _, kb, ke, _) in items} == {32768}
+    # FOLD at 256K with a 4096 window: the far range splits evenly; no item exceeds C.
+    p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=6, mode="fold", n_sink=0, window=4096,
+               max_blocks_per_seq=1 << 14, num_blocks=1 << 15)
+    items, C = da().plan(p, [262144])
+    assert len(items) <= 256 and max(ke - kb for (_, _, kb, ke, _) in items) <= C
+    # Ragged batches: every chunk of a range but the last has one length; the last is no longer.
+    lens = [40000, 300000, 123457]
+    p = params(num_seqs=3, num_q_heads=16, num_kv_heads=4, num_draft_tokens=2, mode="full",
+               max_blocks_per_seq=(300000 + 15) // 16, num_blocks=1 << 20)
+    items, C = da().plan(p, lens)
+    for b in range(3):
+        sizes = [ke - kb for (bb, h, kb, ke, _) in items if bb == b and h == 0]
+        assert sum(sizes) == lens[b] and len(set(sizes[:-1])) <= 1 and sizes[-1] <= sizes[0] <= C
+
+
+def test_chunk_lengths_are_balanced_and_step_aligned():
+    for L in (1, 31, 32, 33, 1000, 4097, 100003):
+        for P in (32, 64, 96, 4096):
+            p = params(num_seqs=1, mode="full", split_keys=P, max_blocks_per_seq=(L + 15) // 16, num_blocks=1 << 16)
+            items, C = da().plan(p, [L])
+            spans = [(kb, ke) for (_, h, kb, ke, _) in items if h == 0]
+            assert spans[0][0] == 0 and spans[-1][1] == L
+            assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
+            assert all((ke - kb) % 32 == 0 for kb, ke in spans[:-1])
+            assert len(spans) == -(-L // P)
 
 
 def test_host_logic_under_sanitizers(tmp_path):
