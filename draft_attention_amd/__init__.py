@@ -169,7 +169,7 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
            debug_visit=None, prof_events=None):
     """Enqueue draft_attn_decode on the current (or given) stream; returns (out, lse).
 
-    q bf16 [B,T,Hq,d]; k_cache / k_side bf16 [NB,Hkv,16,d]; v_cache bf16 [NB,Hkv,d,16];
+    q bf16 [B,T,Hq,d]; k_cache / k_side bf16 [NB,Hkv,d/8,16,8]; v_cache bf16 [NB,Hkv,d,16];
     block_table int32 [B,MB]; ctx_len int32 [B] on the device; ctx_lens: the same
     lengths as a host list (read from ctx_len when omitted, which synchronises).
     out / lse / workspace are allocated with torch when not given.

@@ -95,6 +95,29 @@ __device__ __forceinline__ float pair_add32(float x) {
 }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned int pack_bf16(float lo, float hi) {
+  const bf16x2 h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned int, h);
+}
+
+// P from the score layout to the P.V B operand. pv[4t + r] is this lane's
+// probability for block t of the step at slot 4(g>>1) + 8(g&1) + r. Swapping the
+// upper half-wave of the block-0 values with the lower half-wave of the block-1
+// values leaves lane group g holding slots 8(g&1) .. 8(g&1)+7 of block g>>1 in
+// order: lanes 0-31 keep their block-0 values and receive those of lane+32;
+// lanes 32-63 receive the block-1 values of lane-32 and keep their own.
+__device__ __forceinline__ bf16x8 exchange_p(const float (&pv)[8]) {
+  const unsigned int a0 = pack_bf16(pv[0], pv[1]), a1 = pack_bf16(pv[2], pv[3]);
+  const unsigned int b0 = pack_bf16(pv[4], pv[5]), b1 = pack_bf16(pv[6], pv[7]);
+  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // Items of all sequences before sequence `b` (wave-wide prefix over ctx_len),
 // plus the per-kv-head item counts of `b`. Uniform across the wave.
 struct SeqInfo {
@@ -162,6 +185,9 @@ __device__ void seq_prefix(int32_t b, const int32_t* __restrict__ ctx_len, int32
 // time. Each wave keeps its own online-softmax state; at the end the states
 // are merged through LDS and the workgroup writes one record per query row.
 constexpr int kWaves = 4;
+#ifndef DA_PREFETCH_STEPS
+#define DA_PREFETCH_STEPS 1
+#endif
 
 template <int D>
 struct StepRegs {
@@ -190,10 +216,14 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   const int32_t blk0 = kb >> 4;
   const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
   const int32_t nsteps = (nblk + 1) >> 1;
-  // Key tile t of a step holds keys 8*(i>>2) + 4t + (i&3) at MFMA row i, so the
-  // S^T output lane (row, g) gets keys 8g..8g+3 (t=0) and 8g+4..8g+7 (t=1).
-  const int32_t kslot = 8 * ((i16 >> 2) & 1) + (i16 & 3);
-  const bool khi = (i16 >> 3) != 0;  // key tile rows 8..15 live in the step's second block
+  // Key tile t of a step is block t of the step; MFMA row i reads slot
+  // pi(i) = (i & 3) + 4*((i >> 3) & 1) + 8*((i >> 2) & 1). In the key layout
+  // [c8][slot][8] one load instruction (fixed k-step) then covers channel groups
+  // 4ks..4ks+3 of all 16 slots: 1 KiB contiguous. The S^T output lane (row, g)
+  // holds slots 4(g>>1) + 8(g&1) + r of each block; one permlane32 swap turns
+  // that into slots 8(g&1) .. +7 of block g>>1, the value operand's key order.
+  const int32_t kslot = (i16 & 3) + 4 * ((i16 >> 3) & 1) + 8 * ((i16 >> 2) & 1);
+  const int32_t srel = 4 * (g >> 1) + 8 * (g & 1);  // first slot of this lane's score keys
   const bool vhi = (g >> 1) != 0;    // value keys 8g..8g+7 live in the second block for g >= 2
   const bool sharp = FAR && (a.alpha != 1.f);
   const float alpha = a.alpha;
@@ -212,17 +242,20 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   auto issue = [&](int32_t s, StepRegs<D>& r) {
     r.id0 = sbid[2 * s];
     r.id1 = sbid[2 * s + 1];
-    int32_t kid = khi ? r.id1 : r.id0;
+    // masked block: read block 0 (in bounds), values discarded
+    const int32_t kid0 = r.id0 < 0 ? 0 : r.id0;
+    const int32_t kid1 = r.id1 < 0 ? 0 : r.id1;
     int32_t vid = vhi ? r.id1 : r.id0;
-    kid = kid < 0 ? 0 : kid;  // masked block: read block 0 (in bounds), values discarded
     vid = vid < 0 ? 0 : vid;
-    const __bf16* kp = kpool + ((size_t)((int64_t)kid * a.Hkv + kvh) * 16 + kslot) * D + 8 * g;
+    const size_t krow = (size_t)(g * 16 + kslot) * 8;
+    const __bf16* kp0 = kpool + (size_t)((int64_t)kid0 * a.Hkv + kvh) * (D * 16) + krow;
+    const __bf16* kp1 = kpool + (size_t)((int64_t)kid1 * a.Hkv + kvh) * (D * 16) + krow;
     const __bf16* vp = vpool + ((size_t)((int64_t)vid * a.Hkv + kvh) * D + i16) * 16 + 8 * (g & 1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        r.k[t][ks] = __builtin_nontemporal_load((const bf16x8*)(kp + t * 4 * D + ks * 32));
+    for (int ks = 0; ks < KS; ++ks) {
+      r.k[0][ks] = __builtin_nontemporal_load((const bf16x8*)(kp0 + ks * 512));
+      r.k[1][ks] = __builtin_nontemporal_load((const bf16x8*)(kp1 + ks * 512));
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) r.v[n] = __builtin_nontemporal_load((const bf16x8*)(vp + n * 256));
   };
@@ -269,7 +302,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           float xv = sc[t][rt][rr] * c2;
-          if (!clean && !key_ok(8 * g + 4 * t + rr)) xv = -INFINITY;
+          if (!clean && !key_ok(16 * t + srel + rr)) xv = -INFINITY;
           x[4 * t + rr] = xv;
         }
       float mx = x[0];
@@ -279,7 +312,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
       const float mnew = fmaxf(st.m[rt], mx);
       const float mref = mnew == -INFINITY ? 0.f : mnew;
       const float corr = ex2(st.m[rt] - mref);
-      bf16x8 pb;
+      float pv[8];
       float psum = 0.f;
       if (sharp) {
         const float corr_a = ex2(alpha * (st.m[rt] - mref));
@@ -291,7 +324,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
           const float pa = ex2(alpha * d0);
           psum += p1;
           pasum += pa;
-          pb[e] = (__bf16)pa;
+          pv[e] = pa;
         }
         st.l1[rt] = st.l1[rt] * corr + psum;
         st.l[rt] = st.l[rt] * corr_a + pasum;
@@ -302,13 +335,14 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
         for (int e = 0; e < 8; ++e) {
           const float p = ex2(x[e] - mref);
           psum += p;
-          pb[e] = (__bf16)p;
+          pv[e] = p;
         }
         st.l[rt] = st.l[rt] * corr + psum;
 #pragma unroll
         for (int n = 0; n < NT; ++n) st.o[rt][n] *= corr;
       }
       st.m[rt] = mnew;
+      const bf16x8 pb = exchange_p(pv);
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[n], pb, st.o[rt][n], 0, 0, 0);
@@ -317,6 +351,27 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 
   int32_t s = wave;
   if (s < nsteps) {
+#if DA_PREFETCH_STEPS == 2
+    // Loads run two of this wave's steps ahead of the compute (three buffers).
+    StepRegs<D> ra, rb, rc;
+    issue(s, ra);
+    if (s + kWaves < nsteps) issue(s + kWaves, rb);
+    for (;;) {
+      if (s + 2 * kWaves < nsteps) issue(s + 2 * kWaves, rc);
+      compute(s, ra);
+      s += kWaves;
+      if (s >= nsteps) break;
+      if (s + 2 * kWaves < nsteps) issue(s + 2 * kWaves, ra);
+      compute(s, rb);
+      s += kWaves;
+      if (s >= nsteps) break;
+      if (s + 2 * kWaves < nsteps) issue(s + 2 * kWaves, rb);
+      compute(s, rc);
+      s += kWaves;
+      if (s >= nsteps) break;
+    }
+#else
+    // Loads run one of this wave's steps ahead of the compute (two buffers).
     StepRegs<D> ra, rb;
     issue(s, ra);
     for (;;) {
@@ -329,6 +384,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
       s += kWaves;
       if (s >= nsteps) break;
     }
+#endif
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {

@@ -57,13 +57,16 @@
  * never retains, frees or allocates them.
  *   q            bf16 [B][T][Hq][d], already RoPE-rotated by the caller at
  *                its own positions. 16-byte aligned.
- *   k_cache      bf16 [num_blocks][Hkv][16][d]: rotated keys; 16-token blocks,
- *                slot-major (one key's d channels contiguous). 16-byte aligned.
+ *   k_cache      bf16 [num_blocks][Hkv][d/8][16][8]: rotated keys in 16-token
+ *                blocks; channel 8c + j of the key in slot s sits at [c][s][j], so
+ *                the 16 keys' copies of one 8-channel group are contiguous (256 B)
+ *                and a 64-lane 16-byte load covers 1 KiB contiguous. 16-byte aligned.
  *   v_cache      bf16 [num_blocks][Hkv][d][16]: values, channel-major inside a
  *                block (one channel's 16 slots contiguous), so a 16-byte load
  *                holds eight consecutive keys of one channel. 16-byte aligned.
- *   k_side       bf16 [num_blocks][Hkv][16][d]: unrotated keys, same block ids
- *                as k_cache; read for FOLD's far keys only. NULL unless FOLD.
+ *   k_side       bf16 [num_blocks][Hkv][d/8][16][8]: unrotated keys, same layout
+ *                and block ids as k_cache; read for FOLD's far keys only. NULL
+ *                unless FOLD.
  *   block_table  int32 [B][max_blocks_per_seq]: key j of sequence b lives in
  *                block block_table[b][j / 16], slot j % 16 [WMTP, Builds on:
  *                PagedAttention]. Entries for blocks the mode never reads are

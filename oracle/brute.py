@@ -49,7 +49,7 @@ def rotate(x, pos: float, theta: float):
 
 def _key(pool, table, b, g, j, d):
     blk = int(table[b][j // 16])
-    return [float(pool[blk][g][j % 16][i]) for i in range(d)]
+    return [float(pool[blk][g][i // 8][j % 16][i % 8]) for i in range(d)]
 
 
 def _val(pool, table, b, g, j, d):

@@ -19,8 +19,9 @@ keys (draft tokens do not attend to each other here).
 
 Layouts (the library documents the same ones):
   q           [B, T, Hq, d]      queries, already rotated by the caller
-  k_cache     [NB, Hkv, 16, d]   RoPE-rotated keys, slot-major inside a block
-  k_side      [NB, Hkv, 16, d]   unrotated keys, read for FOLD's far memory
+  k_cache     [NB, Hkv, d/8, 16, 8]  RoPE-rotated keys: within a block, channel
+                                 8c + j of the key in slot s sits at [c, s, j]
+  k_side      [NB, Hkv, d/8, 16, 8]  unrotated keys, read for FOLD's far memory
   v_cache     [NB, Hkv, d, 16]   values, channel-major inside a block
   block_table [B, MB]            key j of sequence b lives in physical block
                                  block_table[b, j // 16] at slot j % 16 [WMTP,
@@ -118,10 +119,11 @@ def rope_rotate(x, pos: float, theta: float) -> np.ndarray:
 
 
 def gather_keys(pool, table_row, idx, kvh: int) -> np.ndarray:
-    """Rows of a slot-major key pool [NB, Hkv, 16, d] for logical keys ``idx`` -> [n, d] fp64."""
+    """Rows of a key pool [NB, Hkv, d/8, 16, 8] for logical keys ``idx`` -> [n, d] fp64."""
     idx = np.asarray(idx, dtype=np.int64)
     blocks = np.asarray(table_row, dtype=np.int64)[idx // BLOCK]
-    return np.asarray(pool[blocks, kvh, idx % BLOCK, :], dtype=np.float64)
+    rows = pool[blocks, kvh, :, idx % BLOCK, :]          # [n, d/8, 8]
+    return np.asarray(rows, dtype=np.float64).reshape(idx.size, pool.shape[2] * pool.shape[4])
 
 
 def gather_values(pool, table_row, idx, kvh: int) -> np.ndarray:
@@ -157,6 +159,8 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int 
     B, T, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     G = Hq // Hkv
+    if k_cache.shape[2] * k_cache.shape[4] != d:
+        raise ValueError("key pool layout must be [NB, Hkv, d/8, 16, 8]")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     out = np.full((B, T, Hq, d), np.nan)
     lse = np.full((B, T, Hq), np.nan)

@@ -5,8 +5,9 @@ attention arithmetic: it only draws random bf16 tensors and lays them out in
 the paged format that the library and the oracle both document:
 
   q           bf16 [B, T, Hq, d]
-  k_cache     bf16 [NB, Hkv, 16, d]   rotated keys, slot-major blocks
-  k_side      bf16 [NB, Hkv, 16, d]   unrotated keys (FOLD far memory), optional
+  k_cache     bf16 [NB, Hkv, d/8, 16, 8]  rotated keys; within a block, channel
+                                      8c + j of slot s sits at [c, s, j]
+  k_side      bf16 [NB, Hkv, d/8, 16, 8]  unrotated keys (FOLD far memory), optional
   v_cache     bf16 [NB, Hkv, d, 16]   values, channel-major blocks
   block_table int32 [B, MB]           -1 past a sequence's last block
   ctx_len     int32 [B]
@@ -69,9 +70,11 @@ def make_inputs(*, ctx_lens, T: int, Hq: int, Hkv: int, d: int, seed: int = 0, d
     spare = perm[used:]
 
     q = _randn_bf16((B, T, Hq, d), dev_gen, device)
-    k = _randn_bf16((NB, Hkv, BLOCK, d), dev_gen, device)
+    if d % 8:
+        raise ValueError("head_dim must be a multiple of 8")
+    k = _randn_bf16((NB, Hkv, d // 8, BLOCK, 8), dev_gen, device)
     v = _randn_bf16((NB, Hkv, d, BLOCK), dev_gen, device)
-    ks = _randn_bf16((NB, Hkv, BLOCK, d), dev_gen, device) if fold else None
+    ks = _randn_bf16((NB, Hkv, d // 8, BLOCK, 8), dev_gen, device) if fold else None
 
     # Needles: chosen logical positions get keys scaled by needle_scale in both key caches.
     if needle_frac > 0:
@@ -82,9 +85,9 @@ def make_inputs(*, ctx_lens, T: int, Hq: int, Hkv: int, d: int, seed: int = 0, d
             pos_j = torch.randperm(L, generator=host)[:cnt]
             blocks = table[b, (pos_j // BLOCK)].long().to(device)
             slots = (pos_j % BLOCK).to(device)
-            k[blocks, :, slots, :] *= needle_scale
+            k[blocks, :, :, slots, :] *= needle_scale
             if ks is not None:
-                ks[blocks, :, slots, :] *= needle_scale
+                ks[blocks, :, :, slots, :] *= needle_scale
 
     fill_val = float("nan") if fill == "nan" else 0.0
     pad_blocks, pad_slot0 = [], []
@@ -93,10 +96,10 @@ def make_inputs(*, ctx_lens, T: int, Hq: int, Hkv: int, d: int, seed: int = 0, d
             pad_blocks.append(int(table[b, L // BLOCK]))
             pad_slot0.append(L % BLOCK)
     for blk, s0 in zip(pad_blocks, pad_slot0):
-        k[blk, :, s0:, :] = fill_val
+        k[blk, :, :, s0:, :] = fill_val
         v[blk, :, :, s0:] = fill_val
         if ks is not None:
-            ks[blk, :, s0:, :] = fill_val
+            ks[blk, :, :, s0:, :] = fill_val
     if spare.numel():
         sp = spare.to(device)
         k[sp] = fill_val

@@ -39,17 +39,17 @@ def paged(ctx_lens, Hkv, d, seed, side=False, shuffle=True, nan_pad=True, spare=
     for b, n in enumerate(nblk):
         table[b, :n] = perm[p:p + n]
         p += n
-    k = rng.standard_normal((NB, Hkv, BLOCK, d))
+    k = rng.standard_normal((NB, Hkv, d // 8, BLOCK, 8))
     v = rng.standard_normal((NB, Hkv, d, BLOCK))
-    ks = rng.standard_normal((NB, Hkv, BLOCK, d)) if side else None
+    ks = rng.standard_normal((NB, Hkv, d // 8, BLOCK, 8)) if side else None
     if nan_pad:
         for b, L in enumerate(ctx_lens):
             if L % BLOCK:
                 blk = table[b, L // BLOCK]
-                k[blk, :, L % BLOCK:, :] = np.nan
+                k[blk, :, :, L % BLOCK:, :] = np.nan
                 v[blk, :, :, L % BLOCK:] = np.nan
                 if side:
-                    ks[blk, :, L % BLOCK:, :] = np.nan
+                    ks[blk, :, :, L % BLOCK:, :] = np.nan
         for blk in perm[sum(nblk):]:
             k[blk] = np.nan
             v[blk] = np.nan
@@ -62,17 +62,28 @@ def repage(keys, vals, d):
     """Pack explicit per-key rows [n, d] into a fresh one-sequence, one-head pool."""
     n = keys.shape[0]
     nb = max((n + BLOCK - 1) // BLOCK, 1)
-    k = np.zeros((nb, 1, BLOCK, d))
+    k = key_pool(nb, 1, d)
     v = np.zeros((nb, 1, d, BLOCK))
     for j in range(n):
-        k[j // BLOCK, 0, j % BLOCK, :] = keys[j]
+        put_key(k, j // BLOCK, 0, j % BLOCK, keys[j])
         v[j // BLOCK, 0, :, j % BLOCK] = vals[j]
     return k, v, np.arange(nb)[None, :]
 
 
+def key_pool(nb, hkv, d):
+    """Zero key pool in the library's layout [NB, Hkv, d/8, 16, 8]."""
+    return np.zeros((nb, hkv, d // 8, BLOCK, 8))
+
+
+def put_key(pool, blk, h, slot, vec):
+    """Write key vector vec[d] into block blk, kv head h, slot: channel 8c + j -> [c, slot, j]."""
+    d = len(vec)
+    pool[blk, h, :, slot, :] = np.asarray(vec, dtype=float).reshape(d // 8, 8)
+
+
 def logical_rows(pool_k, pool_v, table_row, g, L, d):
     """All L logical key/value rows of one sequence, read element by element."""
-    K = np.array([[pool_k[table_row[j // BLOCK], g, j % BLOCK, i] for i in range(d)] for j in range(L)])
+    K = np.array([[pool_k[table_row[j // BLOCK], g, i // 8, j % BLOCK, i % 8] for i in range(d)] for j in range(L)])
     V = np.array([[pool_v[table_row[j // BLOCK], g, i, j % BLOCK] for i in range(d)] for j in range(L)])
     return K.reshape(L, d), V.reshape(L, d)
 
@@ -155,48 +166,61 @@ def test_rope_group_properties_and_complex_form():
 
 # ----------------------------------------------------------------------------- hand-derived cases
 def test_two_key_closed_form():
-    # q = (1, 0), keys (1, 0) and (0, 1), scale 1: logits (1, 0).
-    k = np.zeros((1, 1, BLOCK, 2)); k[0, 0, 0] = [1, 0]; k[0, 0, 1] = [0, 1]
-    v = np.zeros((1, 1, 2, BLOCK)); v[0, 0, :, 0] = [2, 0]; v[0, 0, :, 1] = [0, 4]
-    q = np.array([1.0, 0.0]).reshape(1, 1, 1, 2)
+    # q = e0, keys e0 and e1 (d = 8, other channels 0), scale 1: logits (1, 0).
+    d = 8
+    k = key_pool(1, 1, d)
+    put_key(k, 0, 0, 0, np.eye(d)[0])
+    put_key(k, 0, 0, 1, np.eye(d)[1])
+    v = np.zeros((1, 1, d, BLOCK)); v[0, 0, 0, 0] = 2; v[0, 0, 1, 1] = 4
+    q = np.eye(d)[0].reshape(1, 1, 1, d)
     r = ref.decode(q, k, v, np.array([[0]]), [2], "full", softmax_scale=1.0)
     e = math.e
     assert abs(r["lse"][0, 0, 0] - math.log(e + 1)) < 1e-15
-    assert np.allclose(r["out"][0, 0, 0], [2 * e / (e + 1), 4 / (e + 1)], atol=1e-15)
+    assert np.allclose(r["out"][0, 0, 0], [2 * e / (e + 1), 4 / (e + 1)] + [0] * 6, atol=1e-15)
 
 
 def test_fold_hand_example():
-    # L = 3, W = 1: Loc = {2}, Far = {0, 1}. No rotation, scale 1, q = (1, 0).
+    # L = 3, W = 1: Loc = {2}, Far = {0, 1}. No rotation, scale 1, q = e0.
     # local logit 0; far logits (1, 0); alpha = 2, beta = -1.
     # Z_L = 1, Z_F = e + 1, Z_Fa = e^2 + 1, lse = ln(1 + (e + 1)/e) = ln(2 + 1/e).
     # out = (v2 + e^-1 (e+1) (e^2 v0 + v1)/(e^2 + 1)) / (2 + 1/e)
-    d = 2
-    k = np.zeros((1, 1, BLOCK, d)); ks = np.zeros((1, 1, BLOCK, d))
-    ks[0, 0, 0] = [1, 0]
-    v = np.zeros((1, 1, d, BLOCK)); v[0, 0, :, 0] = [1, 0]; v[0, 0, :, 1] = [0, 1]; v[0, 0, :, 2] = [3, 3]
-    q = np.array([1.0, 0.0]).reshape(1, 1, 1, d)
+    d = 8
+    k = key_pool(1, 1, d)
+    ks = key_pool(1, 1, d)
+    put_key(ks, 0, 0, 0, np.eye(d)[0])
+    v = np.zeros((1, 1, d, BLOCK)); v[0, 0, 0, 0] = 1; v[0, 0, 1, 1] = 1; v[0, 0, :2, 2] = 3
+    q = np.eye(d)[0].reshape(1, 1, 1, d)
     r = ref.decode(q, k, v, np.array([[0]]), [3], "fold", window=1, alpha=2.0, beta=-1.0,
                    softmax_scale=1.0, rope="none", k_side=ks)
     e = math.e
     den = 2 + 1 / e
     far = (e + 1) / e / (e * e + 1)
-    want = (np.array([3.0, 3.0]) + far * np.array([e * e, 1.0])) / den
+    want = (np.array([3.0, 3.0] + [0] * 6) + far * np.array([e * e, 1.0] + [0] * 6)) / den
     assert abs(r["lse"][0, 0, 0] - math.log(den)) < 1e-15
     assert np.allclose(r["out"][0, 0, 0], want, atol=1e-15)
 
 
-def test_value_layout_is_channel_major():
-    # Key j, channel i holds 1000 j + i. A window of one key picks key L - 1.
-    d, L = 4, 21
-    k = np.zeros((2, 1, BLOCK, d)); v = np.zeros((2, 1, d, BLOCK))
+def test_key_and_value_layouts():
+    # Value: key j, channel i holds 1000 j + i. A window of one key picks key L - 1.
+    d, L = 8, 21
+    k = key_pool(2, 1, d); v = np.zeros((2, 1, d, BLOCK))
     for j in range(L):
         for i in range(d):
             v[j // BLOCK, 0, i, j % BLOCK] = 1000 * j + i
     q = np.zeros((1, 1, 1, d))
     r = ref.decode(q, k, v, np.array([[0, 1]]), [L], "window", window=1, n_sink=0)
-    assert np.array_equal(r["out"][0, 0, 0], [20000, 20001, 20002, 20003])
+    assert np.array_equal(r["out"][0, 0, 0], [20000 + i for i in range(d)])
     r = ref.decode(q, k, v, np.array([[1, 0]]), [L], "window", window=1, n_sink=0)
     assert np.array_equal(r["out"][0, 0, 0], [1000 * 4 + i for i in range(d)])  # block swap: key 20 -> blk 0 slot 4
+    # Key: channel 8c + j of slot s sits at [c, s, j]; one key (slot 5 of block 0) with channel 11 set.
+    d = 16
+    k = key_pool(1, 1, d)
+    k[0, 0, 1, 5, 3] = 2.0                      # channel 8*1 + 3 = 11 of slot 5
+    v = np.zeros((1, 1, d, BLOCK)); v[0, 0, 0, :6] = np.arange(6)
+    q = np.zeros((1, 1, 1, d)); q[0, 0, 0, 11] = 1.0
+    r = ref.decode(q, k, v, np.array([[0]]), [6], "full", softmax_scale=1.0)
+    # logits: 2 for key 5, 0 otherwise -> lse = ln(5 + e^2)
+    assert abs(r["lse"][0, 0, 0] - math.log(5 + math.e ** 2)) < 1e-14
 
 
 # ----------------------------------------------------------------------------- brute force

@@ -15,7 +15,7 @@ def test_layout_padding_and_determinism():
         assert torch.equal(torch.nan_to_num(a[key].float(), 123.0), torch.nan_to_num(b[key].float(), 123.0))
     assert a["q"].shape == (4, 2, 4, 8) and a["q"].dtype == torch.bfloat16
     NB = 3 + 1 + 0 + 4 + 2
-    assert a["k_cache"].shape == (NB, 2, 16, 8)
+    assert a["k_cache"].shape == (NB, 2, 1, 16, 8)
     assert a["v_cache"].shape == (NB, 2, 8, 16)
     t = a["block_table"]
     assert t.shape == (4, 4) and t.dtype == torch.int32
@@ -24,10 +24,10 @@ def test_layout_padding_and_determinism():
     assert t[2].tolist() == [-1] * 4 and t[1, 1:].tolist() == [-1] * 3
     # slots past L are NaN, slots below L are finite
     blk = int(t[0, 2])
-    assert torch.isnan(a["k_cache"][blk, :, 5:, :].float()).all()
-    assert torch.isfinite(a["k_cache"][blk, :, :5, :].float()).all()
+    assert torch.isnan(a["k_cache"][blk, :, :, 5:, :].float()).all()
+    assert torch.isfinite(a["k_cache"][blk, :, :, :5, :].float()).all()
     assert torch.isnan(a["v_cache"][blk, :, :, 5:].float()).all()
-    assert torch.isnan(a["k_side"][blk, :, 5:, :].float()).all()
+    assert torch.isnan(a["k_side"][blk, :, :, 5:, :].float()).all()
     spare = sorted(set(range(NB)) - set(used))
     assert all(torch.isnan(a["k_cache"][s].float()).all() for s in spare)
     c = synth.make_inputs(ctx_lens=[37, 16, 0, 50], T=2, Hq=4, Hkv=2, d=8, seed=4, fold=True)
@@ -47,8 +47,8 @@ def test_needles_scale_keys_in_both_caches():
     x = synth.make_inputs(needle_frac=0.01, **kw)
     y = synth.make_inputs(needle_frac=0.0, **kw)
     for key in ("k_cache", "k_side"):
-        a = x[key].float().reshape(-1, 16)
-        b = y[key].float().reshape(-1, 16)
+        a = x[key].float().permute(0, 1, 3, 2, 4).reshape(-1, 16)   # one row per (block, head, slot)
+        b = y[key].float().permute(0, 1, 3, 2, 4).reshape(-1, 16)
         scaled = torch.all(a == 8 * b, dim=1) & torch.any(b != 0, dim=1)
         same = torch.all(a == b, dim=1)
         assert torch.all(scaled | same)
