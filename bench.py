@@ -3,7 +3,10 @@
 
 One step = one draft_attn_decode call: the device-side work decomposition, the
 split-K streaming pass over every visible K/V block and the log-sum-exp merge.
-Inputs (seeded, synthetic, bf16) are resident in HBM before timing starts.
+Inputs (seeded, synthetic, bf16) are resident in HBM before timing starts. Each
+timed step is one eager call through a prepared binding (arguments marshalled
+once, one C call per step). --graph instead times replays of the call captured
+in a HIP graph; on this software stack a replay costs more than an eager call.
 
 Default workload: the million-token draft step (1 sequence, 2^20 cached keys in
 16-token blocks behind a shuffled block table, 32 query / 8 kv heads, d = 128,
@@ -50,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the call captured in a HIP graph instead of eager calls")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -106,7 +111,7 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes": n, "launches": 3}), flush=True)
 
 
-def time_workload(w, kw, steps, warmup, seed, split, want_events=True):
+def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False):
     """Generate inputs on the GPU, time `steps` decode calls; returns a result dict."""
     import torch
 
@@ -128,20 +133,23 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True):
     ev = HipEvents() if want_events else None
     pairs = [(ev.create(), ev.create()) for _ in range(steps)] if ev else [None] * steps
 
+    call = da.prepare(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], k_side=side,
+                      ctx_lens=w.ctx_lens, out=out, lse=lse, workspace=ws, rope_theta=w.rope_theta,
+                      split_keys=split, **kw)
+
     def step(pe):
-        da.decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], k_side=side,
-                  ctx_lens=w.ctx_lens, out=out, lse=lse, workspace=ws, rope_theta=w.rope_theta,
-                  split_keys=split, prof_events=pe, **kw)
+        call(prof_events=pe)
 
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    # Eager steps, with the streaming pass bracketed by HIP events.
     t0 = time.perf_counter()
     for k in range(steps):
         step(pairs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
+    ms_eager = (t1 - t0) * 1e3 / steps
     pass1 = None
     if ev:
         durs = [ev.elapsed_ms(a, b) for a, b in pairs]
@@ -149,9 +157,32 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True):
         for a, b in pairs:
             ev.destroy(a)
             ev.destroy(b)
+    ms = ms_eager
+    ms_graph = None
+    if graph:
+        # One step captured in a HIP graph and replayed: the whole call's GPU work
+        # without the host's per-call launch cost, as a serving loop runs it.
+        side_stream = torch.cuda.Stream()
+        side_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side_stream):
+            step(None)
+        torch.cuda.current_stream().wait_stream(side_stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(None)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_graph = ms = (t1 - t0) * 1e3 / steps
+        del g
     keys = sum(visible_keys(L, **kw) for L in w.ctx_lens) * w.Hkv
     bytes_ = keys * 4 * w.d
-    res = dict(x=x, kw=kw, ms=ms, pass1_ms=pass1, bytes=bytes_, keys=keys // w.Hkv, chunk=chunk,
+    res = dict(x=x, kw=kw, ms=ms, ms_eager=ms_eager, pass1_ms=pass1, bytes=bytes_, keys=keys // w.Hkv, chunk=chunk,
                torch_ok=bool(torch.isfinite(out).all().item()))
     return res
 
@@ -214,14 +245,15 @@ def main():
     wl = synth.workloads(args.seed)
     w = wl[args.workload]
     kw = w.runs[args.run]
-    r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys)
+    r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys, graph=args.graph)
     gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
     p1 = r["bytes"] / (r["pass1_ms"] * 1e-3) / 1e9
     tag = f"{w.name}/{kw['mode']}"
     secondary = {}
     if not args.no_secondary and w.name == "needles_1m":
         w2 = wl["llama8b_128k"]
-        r2 = time_workload(w2, w2.runs[0], args.steps, args.warmup, args.seed, 0, want_events=False)
+        r2 = time_workload(w2, w2.runs[0], args.steps, args.warmup, args.seed, 0, want_events=False,
+                           graph=args.graph)
         secondary["llama8b_128k/full"] = dict(ms_per_step=round(r2["ms"], 5),
                                               draft_steps_per_s=round(1e3 / r2["ms"], 1),
                                               kv_gbs=round(r2["bytes"] / (r2["ms"] * 1e-3) / 1e9, 1))
@@ -239,6 +271,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 5),
+        "ms_per_step_eager": round(r["ms_eager"], 5),
+        "timing": "replays of one call captured in a HIP graph" if args.graph else "eager calls",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

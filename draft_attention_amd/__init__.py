@@ -163,6 +163,62 @@ def plan(params: Params, ctx_lens):
     return items, int(chunk.value)
 
 
+class PreparedDecode:
+    """One decode call with its arguments marshalled once; calling it enqueues the
+    call again on the stream given at preparation (or on `stream`)."""
+
+    def __init__(self, params, args, out, lse, keep):
+        self.params, self.args, self.out, self.lse, self._keep = params, args, out, lse, keep
+
+    def __call__(self, stream=None, prof_events=None):
+        p = self.params
+        if prof_events is not None:
+            p.prof_events[0], p.prof_events[1] = int(prof_events[0]), int(prof_events[1])
+        else:
+            p.prof_events[0] = p.prof_events[1] = None
+        args = self.args if stream is None else self.args[:-1] + (int(stream),)
+        st = lib.draft_attn_decode(ctypes.byref(p), *args)
+        if st != OK:
+            raise DraftAttnError(st, "draft_attn_decode")
+        return self.out, self.lse
+
+
+def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
+            beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
+            ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
+            debug_visit=None) -> PreparedDecode:
+    """Marshal the arguments of decode() once (same meaning as there)."""
+    import torch
+
+    B, T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if ctx_lens is None:
+        ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
+    visit_ptr, visit_stride = 0, 0
+    if debug_visit is not None:
+        visit_ptr, visit_stride = debug_visit.data_ptr(), debug_visit.shape[1]
+    p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                    num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
+                    window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
+                    softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
+                    split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    need = workspace_size(p, ctx_lens)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    host = _host_i32(ctx_lens)
+    args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side), ptr(block_table), ptr(ctx_len), host, ptr(out),
+            ptr(lse), ptr(workspace), workspace.numel() * workspace.element_size(), s)
+    keep = (q, k_cache, v_cache, k_side, block_table, ctx_len, workspace, debug_visit, host)
+    return PreparedDecode(p, args, out, lse, keep)
+
+
 def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
            beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
            ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,

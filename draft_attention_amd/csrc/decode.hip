@@ -427,26 +427,13 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
   int32_t kb, ke, part;
   item_bounds(rg, kidx, a.C, &kb, &ke, &part);
 
-  // Block ids of the chunk, validated, plus one pad entry for the last step's pair.
-  const int32_t blk0 = kb >> 4;
-  const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
-  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  for (int32_t j = tid; j < nblk + 1; j += 256) {
-    int32_t id = -1;
-    if (j < nblk && blk0 + j < a.max_blocks) {
-      id = trow[blk0 + j];
-      if (id < 0 || id >= a.num_blocks) id = -1;
-    }
-    sbid[j] = id;
-  }
-  __syncthreads();
-
   // Logit scale in the log2 domain: softmax_scale * s(n) * log2(e).
   const int32_t n = visible_count(L, a.mode, a.W, a.S);
   const double sn = 1.0 + (double)a.kappa * log((double)(n > a.n0 ? n : a.n0) / (double)a.n0);
   const float c2 = (float)((double)a.scale * sn * 1.4426950408889634);
 
-  // Query rows of this kv head: row = t * G + (h - kvh * G), zero-padded to 16 * RT.
+  // Query rows of this kv head (loaded before the block table so both loads are
+  // in flight together): row = t * G + (h - kvh * G), zero-padded to 16 * RT.
   bf16x8 qh[RT][KS], ql[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -464,6 +451,20 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
       ql[rt][ks] = z;
     }
   }
+
+  // Block ids of the chunk, validated, plus one pad entry for the last step's pair.
+  const int32_t blk0 = kb >> 4;
+  const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
+  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  for (int32_t j = tid; j < nblk + 1; j += 256) {
+    int32_t id = -1;
+    if (j < nblk && blk0 + j < a.max_blocks) {
+      id = trow[blk0 + j];
+      if (id < 0 || id >= a.num_blocks) id = -1;
+    }
+    sbid[j] = id;
+  }
+  __syncthreads();
 
   WaveState<D, RT> st;
   const bool far_part = FOLDK && part == kPartFar;

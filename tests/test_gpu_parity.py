@@ -263,3 +263,44 @@ def test_full_size_batch16_ragged():
     w = synth.workloads()["batch16_ragged"]
     for kw in w.runs:
         _sampled(w, kw, pairs=[(0, 2), (7, 2), (15, 6)])
+
+
+def test_graph_replay_matches_eager():
+    # The call captured in a HIP graph, replayed several times with eager work in
+    # between; every replay must equal the eager result bit for bit.
+    da = _da()
+    x = synth.make_inputs(ctx_lens=[7000, 333], T=4, Hq=16, Hkv=4, d=128, seed=21, fold=True)
+    g = to_dev(x)
+    kw = dict(mode="fold", window=1024, alpha=2.0, beta=-1.0, kappa=0.1, n0=256)
+    out = torch.empty((2, 4, 16, 128), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((2, 4, 16), dtype=torch.float32, device="cuda:0")
+    p = da.make_params(num_seqs=2, num_draft_tokens=4, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                       num_blocks=g["k_cache"].shape[0], max_blocks_per_seq=g["block_table"].shape[1], **kw)
+    ws = torch.empty(da.workspace_size(p, g["ctx_lens"]), dtype=torch.uint8, device="cuda:0")
+
+    def call():
+        da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=g["k_side"],
+                  ctx_lens=g["ctx_lens"], out=out, lse=lse, workspace=ws, rope_theta=5e5, **kw)
+
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(0xAB)                      # the workspace's contents on entry must not matter
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {i}"
+        eager = (g["q"].float() * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(eager)
