@@ -54,6 +54,23 @@ class Params(ctypes.Structure):
     ]
 
 
+class AppendParams(ctypes.Structure):
+    """Mirror of draft_attn_append_params."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_new", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("rope", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+    ]
+
+
 class DraftAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {strerror(status)} (status {status})")
@@ -81,14 +98,19 @@ def _load():
     lib.draft_attn_decode.restype = ctypes.c_int
     lib.draft_attn_plan.argtypes = [P, i32p, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), i32p]
     lib.draft_attn_plan.restype = ctypes.c_int
+    AP = ctypes.POINTER(AppendParams)
+    lib.draft_attn_append_params_init.argtypes = [AP]
+    lib.draft_attn_append_params_init.restype = None
+    lib.draft_attn_append.argtypes = [AP, vp, vp, vp, vp, i32p, vp, vp, vp, vp]
+    lib.draft_attn_append.restype = ctypes.c_int
     lib.draft_attn_strerror.argtypes = [ctypes.c_int]
     lib.draft_attn_strerror.restype = ctypes.c_char_p
     lib.draft_attn_version.argtypes = []
     lib.draft_attn_version.restype = ctypes.c_int
     if lib.draft_attn_version() != ABI_VERSION:
         raise ImportError("libdraft_attn.so ABI version mismatch")
-    if ctypes.sizeof(Params) != 120:
-        raise ImportError("Params mirror has the wrong size")
+    if ctypes.sizeof(Params) != 120 or ctypes.sizeof(AppendParams) != 48:
+        raise ImportError("params mirror has the wrong size")
     return lib
 
 
@@ -261,3 +283,33 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
     if st != OK:
         raise DraftAttnError(st, "draft_attn_decode")
     return out, lse
+
+
+def make_append_params(*, num_seqs, num_new, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
+                       rope="neox", rope_theta=1e4) -> AppendParams:
+    p = AppendParams()
+    lib.draft_attn_append_params_init(ctypes.byref(p))
+    p.num_seqs, p.num_new, p.num_kv_heads, p.head_dim = int(num_seqs), int(num_new), int(num_kv_heads), int(head_dim)
+    p.num_blocks, p.max_blocks_per_seq = int(num_blocks), int(max_blocks_per_seq)
+    p.rope = _ROPES[rope] if isinstance(rope, str) else int(rope)
+    p.rope_theta = float(rope_theta)
+    return p
+
+
+def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, *, rope="neox", rope_theta=1e4,
+           pos_host=None, stream=None):
+    """Enqueue draft_attn_append: write k_new / v_new ([B, n_new, Hkv, d] bf16) at positions
+    pos[b] + i (pos: int32 [B] on the device; pos_host: the same values as a list)."""
+    import torch
+
+    B, n_new, Hkv, d = k_new.shape
+    if pos_host is None:
+        pos_host = [int(x) for x in pos.cpu().tolist()]
+    p = make_append_params(num_seqs=B, num_new=n_new, num_kv_heads=Hkv, head_dim=d, num_blocks=k_cache.shape[0],
+                           max_blocks_per_seq=block_table.shape[1], rope=rope, rope_theta=rope_theta)
+    s = torch.cuda.current_stream(k_new.device).cuda_stream if stream is None else int(stream)
+    st = lib.draft_attn_append(ctypes.byref(p), k_new.data_ptr(), v_new.data_ptr(), block_table.data_ptr(),
+                               pos.data_ptr(), _host_i32(pos_host), k_cache.data_ptr(), v_cache.data_ptr(),
+                               None if k_side is None else k_side.data_ptr(), s)
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_append")

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdraft_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-HIP_SOURCES = [os.path.join(HERE, "csrc", "decode.hip")]
+HIP_SOURCES = [os.path.join(HERE, "csrc", "decode.hip"), os.path.join(HERE, "csrc", "append.hip")]
 CXX_SOURCES = [os.path.join(HERE, "csrc", "host.cpp")]  # pure C++: built by the host compiler
 
 # Packed fp32 VALU ops are turned off for all device code.

@@ -144,9 +144,36 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   return DRAFT_ATTN_OK;
 }
 
+int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host) {
+  if (!p) return DRAFT_ATTN_EINVAL;
+  if (p->struct_size != sizeof(draft_attn_append_params) || p->reserved != 0) return DRAFT_ATTN_EINVAL;
+  if (p->num_seqs < 0 || p->num_new < 1 || p->num_kv_heads < 1 || p->head_dim < 1) return DRAFT_ATTN_EINVAL;
+  if (p->block_size != kBlock || p->max_blocks_per_seq < 1 || p->num_blocks < 0) return DRAFT_ATTN_EINVAL;
+  if (p->rope != DRAFT_ATTN_ROPE_NEOX && p->rope != DRAFT_ATTN_ROPE_NONE) return DRAFT_ATTN_EINVAL;
+  if (p->rope == DRAFT_ATTN_ROPE_NEOX && (!finite_f(p->rope_theta) || !(p->rope_theta > 0.0))) return DRAFT_ATTN_EINVAL;
+  if (p->num_seqs > 0 && (!pos_host || p->num_blocks < 1)) return DRAFT_ATTN_EINVAL;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    if (pos_host[b] < 0) return DRAFT_ATTN_EINVAL;
+    if ((int64_t)pos_host[b] + p->num_new > (int64_t)p->max_blocks_per_seq * kBlock) return DRAFT_ATTN_EINVAL;
+  }
+  if (p->head_dim != 64 && p->head_dim != 128) return DRAFT_ATTN_ENOTSUP;
+  if ((int64_t)p->num_seqs * p->num_new * p->num_kv_heads * (p->head_dim / 16) > (int64_t)0x7fffffff * 256)
+    return DRAFT_ATTN_EINVAL;
+  return DRAFT_ATTN_OK;
+}
+
 }  // namespace da
 
 extern "C" {
+
+void draft_attn_append_params_init(draft_attn_append_params* p) {
+  if (!p) return;
+  memset(p, 0, sizeof(*p));
+  p->struct_size = sizeof(draft_attn_append_params);
+  p->block_size = 16;
+  p->rope = DRAFT_ATTN_ROPE_NEOX;
+  p->rope_theta = 1e4;
+}
 
 void draft_attn_params_init(draft_attn_params* p) {
   if (!p) return;

@@ -25,4 +25,7 @@ struct Prepared {
 // size and sizes the workspace. Returns a DRAFT_ATTN_* status.
 int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* out);
 
+// Checks the scalar arguments and host positions of draft_attn_append.
+int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host);
+
 }  // namespace da

@@ -184,6 +184,44 @@ int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_c
 int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t* items,
                     int64_t capacity, int64_t* n_items, int32_t* chunk_keys);
 
+/* ---------------------------------------------------------------------------
+ * KV append with FOLD side-cache bookkeeping. For token i < num_new of sequence
+ * b, at position p = pos[b] + i, in block block_table[b][p / 16] and slot p % 16:
+ *   k_cache <- R(p) k_new[b][i]  rounded to bf16 (to nearest, ties to even) from
+ *                                the fp64 rotation; with DRAFT_ATTN_ROPE_NONE the
+ *                                key is copied unchanged
+ *   k_side  <- k_new[b][i]       (when k_side is not NULL)
+ *   v_cache <- v_new[b][i]
+ * R(p) is the NeoX rotation of the header above at angle p * rope_theta^(-2i/d).
+ * The unrotated side cache is what FOLD's far memory reads ["FOLD: Position-Free
+ * Far Memory with Local Order for Long-Context Speculative Decoding", review].
+ * k_new, v_new: bf16 [B][num_new][Hkv][d] device, 16-byte aligned; pos_dev /
+ * pos_host: int32 [B] on device / host with the same values; caches as for
+ * draft_attn_decode. Every written block must be allocated in block_table; a
+ * token whose table entry lies outside [0, num_blocks) is not written. Nothing
+ * outside the new tokens' slots is touched. Validation is host-side and runs
+ * before anything is enqueued. */
+typedef struct draft_attn_append_params {
+  uint32_t struct_size;        /* sizeof(draft_attn_append_params) */
+  int32_t num_seqs;            /* B >= 0 */
+  int32_t num_new;             /* tokens appended per sequence, >= 1 */
+  int32_t num_kv_heads;        /* Hkv >= 1 */
+  int32_t head_dim;            /* 64 or 128 */
+  int32_t block_size;          /* must be 16 */
+  int32_t num_blocks;          /* physical blocks in each pool */
+  int32_t max_blocks_per_seq;  /* row stride of block_table; pos + num_new <= 16 * it */
+  int32_t rope;                /* DRAFT_ATTN_ROPE_NEOX or _NONE */
+  int32_t reserved;            /* must be 0 */
+  double rope_theta;           /* finite, > 0 with NEOX */
+} draft_attn_append_params;
+
+/* Defaults: block_size 16, NEOX with rope_theta 1e4, struct_size set. */
+void draft_attn_append_params_init(draft_attn_append_params* p);
+
+int draft_attn_append(const draft_attn_append_params* p, const void* k_new, const void* v_new,
+                      const int32_t* block_table, const int32_t* pos_dev, const int32_t* pos_host,
+                      void* k_cache, void* v_cache, void* k_side, void* stream);
+
 /* Static description of a status code. */
 const char* draft_attn_strerror(int status);
 

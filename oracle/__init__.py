@@ -26,6 +26,8 @@ pinned against anything printed on the pages.
 from . import reference, brute  # noqa: F401
 from .reference import (  # noqa: F401
     MODES,
+    append,
+    bf16_round,
     decode,
     index_sets,
     visible_count,

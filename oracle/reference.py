@@ -210,3 +210,56 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int 
     if details:
         res["details"] = info
     return res
+
+
+# ----------------------------------------------------------------------------- cache append
+def bf16_round(x) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value (ties to even), returned as fp64.
+
+    Written from the definition: with e = floor(log2|x|), bf16 spacing near x is
+    2^(e-7); the two neighbours are exact dyadic numbers, so comparing distances
+    in fp64 is exact. Zero stays zero; finite inputs in the normal range only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = x != 0
+    xs = x[nz]
+    _, e = np.frexp(np.abs(xs))            # |x| = f * 2^e with f in [0.5, 1)
+    ulp = np.ldexp(1.0, e - 8)              # 8 significant bits
+    lo = np.floor(xs / ulp) * ulp
+    hi = lo + ulp
+    dlo, dhi = xs - lo, hi - xs
+    lo_even = (np.floor(xs / ulp) % 2) == 0
+    out[nz] = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo_even, lo, hi)))
+    return out
+
+
+def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, rope: str = "neox",
+           rope_theta: float = 1e4):
+    """Write newly accepted tokens into the paged caches; returns updated copies.
+
+    Token i of sequence b sits at position p = pos[b] + i, in block
+    block_table[b, p // 16] at slot p % 16. The rotated cache receives the key
+    turned to its own position, R(p) k, rounded to bf16; the side cache keeps the
+    unrotated key for FOLD's far memory ("FOLD: Position-Free Far Memory with
+    Local Order for Long-Context Speculative Decoding", review: the unrotated
+    side cache and its bookkeeping); the value cache receives v. k_new, v_new:
+    [B, n_new, Hkv, d] (bf16 values as fp64).
+    """
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    B, n_new, Hkv, d = k_new.shape
+    kc, vc = np.array(k_cache, dtype=np.float64), np.array(v_cache, dtype=np.float64)
+    ks = None if k_side is None else np.array(k_side, dtype=np.float64)
+    for b in range(B):
+        for i in range(n_new):
+            p = int(pos[b]) + i
+            blk, slot = int(block_table[b][p // BLOCK]), p % BLOCK
+            for h in range(Hkv):
+                raw = k_new[b, i, h]
+                rot = bf16_round(rope_rotate(raw, p, rope_theta)) if rope == "neox" else raw
+                kc[blk, h, :, slot, :] = rot.reshape(d // 8, 8)
+                if ks is not None:
+                    ks[blk, h, :, slot, :] = raw.reshape(d // 8, 8)
+                vc[blk, h, :, slot] = v_new[b, i, h]
+    return kc, vc, ks

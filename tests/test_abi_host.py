@@ -53,6 +53,56 @@ def test_params_layout_matches_the_c_compiler(tmp_path):
         assert getattr(da().Params, f).offset == off, f
 
 
+def test_append_params_layout_matches_the_c_compiler(tmp_path):
+    fields = [f for f, _ in da().AppendParams._fields_]
+    src = tmp_path / "alayout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void) {',
+             'printf("%zu\\n", sizeof(draft_attn_append_params));']
+    lines += [f'printf("%zu\\n", offsetof(draft_attn_append_params, {f}));' for f in fields]
+    lines += ['return 0; }']
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "alayout"
+    subprocess.run(["gcc", "-std=c99", str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(da().AppendParams)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(da().AppendParams, f).offset == off, f
+
+
+def _append_call(p, pos=(0, 5), **ptrs):
+    P = dict(k=0x10000, v=0x20000, table=0x30000, posd=0x40000, kc=0x50000, vc=0x60000, ks=None)
+    P.update(ptrs)
+    host = (ctypes.c_int32 * max(len(pos), 1))(*pos)
+    return da().lib.draft_attn_append(ctypes.byref(p), P["k"], P["v"], P["table"], P["posd"], host, P["kc"], P["vc"],
+                                      P["ks"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=-1), -1), (dict(num_new=0), -1), (dict(num_kv_heads=0), -1), (dict(head_dim=96), -4),
+    (dict(max_blocks_per_seq=0), -1), (dict(rope=7), -1), (dict(rope_theta=-1.0), -1), (dict(num_blocks=0), -1),
+])
+def test_append_validation(kw, status):
+    base = dict(num_seqs=2, num_new=4, num_kv_heads=2, head_dim=128, num_blocks=16, max_blocks_per_seq=4)
+    base.update(kw)
+    assert _append_call(da().make_append_params(**base)) == status
+
+
+def test_append_positions_pointers_and_alignment():
+    mk = lambda **kw: da().make_append_params(**dict(dict(num_seqs=2, num_new=4, num_kv_heads=2, head_dim=128,
+                                                          num_blocks=16, max_blocks_per_seq=4), **kw))
+    assert _append_call(mk(), pos=(-1, 0)) == -1
+    assert _append_call(mk(), pos=(61, 0)) == -1            # 61 + 4 > 64 slots
+    for name in ("k", "v", "table", "posd", "kc", "vc"):
+        assert _append_call(mk(), **{name: None}) == -1, name
+    assert _append_call(mk(), k=0x10008) == -1
+    assert _append_call(mk(), ks=0x70004) == -1
+    p = mk()
+    p.reserved = 3
+    assert _append_call(p) == -1
+    assert _append_call(mk(num_seqs=0), pos=()) == 0
+    assert _append_call(mk(rope="none", rope_theta=0.0), pos=(0, 0), k=None) == -1   # theta unused, pointer checked
+
+
 def test_status_strings():
     for st in (0, -1, -2, -3, -4):
         assert da().strerror(st) and da().strerror(st) != "unknown status"

@@ -1,0 +1,132 @@
+"""GPU parity of the KV append (draft_attn_append) against the oracle.
+
+The bar is bit equality of all three pools: the side cache and the values are
+copies, and the rotated key is the correctly rounded bf16 value of the fp64
+rotation on both sides. Pool slots the append must not touch hold NaN, so any
+stray write shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _da():
+    import draft_attention_amd as da
+    return da
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().double().numpy()
+
+
+def _pools_equal(a, b):
+    return np.array_equal(a, b, equal_nan=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rope,side", [("neox", True), ("none", True), ("neox", False)])
+def test_append_matches_oracle_bit_for_bit(d, rope, side):
+    da = _da()
+    dev = torch.device("cuda:0")
+    lens = [40, 3, 200]                      # existing lengths: appends start mid-block and at block 0
+    n_new, Hkv = 11, 4
+    x = synth.make_inputs(ctx_lens=[L + n_new for L in lens], T=1, Hq=Hkv, Hkv=Hkv, d=d, seed=31, fold=True)
+    g = torch.Generator().manual_seed(5)
+    kn = (torch.randn((3, n_new, Hkv, d), generator=g) * 3).to(torch.bfloat16)
+    vn = torch.randn((3, n_new, Hkv, d), generator=g).to(torch.bfloat16)
+    kc, vc, ks = x["k_cache"].to(dev), x["v_cache"].to(dev), x["k_side"].to(dev)
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    da.append(kn.to(dev), vn.to(dev), x["block_table"].to(dev), pos, kc, vc, ks if side else None, rope=rope,
+              rope_theta=5e5, pos_host=lens)
+    torch.cuda.synchronize()
+    rk, rv, rs = oracle.append(_np(kn), _np(vn), x["block_table"].numpy(), lens, _np(x["k_cache"]),
+                               _np(x["v_cache"]), _np(x["k_side"]) if side else None, rope=rope, rope_theta=5e5)
+    assert _pools_equal(_np(kc), rk)
+    assert _pools_equal(_np(vc), rv)
+    if side:
+        assert _pools_equal(_np(ks), rs)
+    else:
+        assert _pools_equal(_np(ks), _np(x["k_side"]))
+
+
+def test_append_far_positions_and_unallocated_blocks():
+    # Positions near 2^20 (angles up to ~1e6 rad), and a token whose block is not
+    # allocated (-1 table entry): nothing is written for it.
+    da = _da()
+    dev = torch.device("cuda:0")
+    d, Hkv, n_new = 128, 2, 20
+    MB = 65536
+    start = (1 << 20) - 37
+    blocks = list(range(start // 16, (start + n_new - 1) // 16 + 1))
+    NB = len(blocks) + 1
+    table = torch.full((1, MB), -1, dtype=torch.int32)
+    for i, j in enumerate(blocks[:-1]):                     # the last block stays unallocated
+        table[0, j] = i
+    kc = torch.full((NB, Hkv, d // 8, 16, 8), float("nan"), dtype=torch.bfloat16)
+    vc = torch.full((NB, Hkv, d, 16), float("nan"), dtype=torch.bfloat16)
+    ks = kc.clone()
+    g = torch.Generator().manual_seed(6)
+    kn = torch.randn((1, n_new, Hkv, d), generator=g).to(torch.bfloat16)
+    vn = torch.randn((1, n_new, Hkv, d), generator=g).to(torch.bfloat16)
+    gk, gv, gs = kc.to(dev), vc.to(dev), ks.to(dev)
+    da.append(kn.to(dev), vn.to(dev), table.to(dev), torch.tensor([start], dtype=torch.int32, device=dev),
+              gk, gv, gs, rope="neox", rope_theta=5e5, pos_host=[start])
+    torch.cuda.synchronize()
+    keep = [i for i in range(n_new) if (start + i) // 16 != blocks[-1]]
+    rk, rv, rs = oracle.append(_np(kn)[:, keep], _np(vn)[:, keep], np.where(table.numpy() < 0, 0, table.numpy()),
+                               [start], _np(kc), _np(vc), _np(ks), rope="neox", rope_theta=5e5)
+    assert len(keep) < n_new
+    assert _pools_equal(_np(gk), rk) and _pools_equal(_np(gv), rv) and _pools_equal(_np(gs), rs)
+
+
+def test_cache_built_by_appends_then_decoded():
+    # Prefill three sequences entirely through the append kernel (chunks of 64 and
+    # a ragged tail), check the pools against the oracle's appends, then decode
+    # full and FOLD on the GPU-built cache against the oracle on its own cache.
+    da = _da()
+    dev = torch.device("cuda:0")
+    lens = [1000, 77, 2500]
+    d, Hkv, Hq, T = 128, 2, 8, 4
+    x = synth.make_inputs(ctx_lens=lens, T=T, Hq=Hq, Hkv=Hkv, d=d, seed=41, fold=True)
+    g = torch.Generator().manual_seed(7)
+    total = max(lens)
+    kr = torch.randn((3, total, Hkv, d), generator=g).to(torch.bfloat16)
+    vr = torch.randn((3, total, Hkv, d), generator=g).to(torch.bfloat16)
+    kc, vc, ks = x["k_cache"].to(dev), x["v_cache"].to(dev), x["k_side"].to(dev)
+    table = x["block_table"].to(dev)
+    rk, rv, rs = _np(x["k_cache"]), _np(x["v_cache"]), _np(x["k_side"])
+    done = [0, 0, 0]
+    while any(done[b] < lens[b] for b in range(3)):
+        # every sequence appends the same number of tokens per call; finished ones
+        # append into positions past their length in their own (spare) capacity
+        chunk = 64
+        for b in range(3):
+            if done[b] >= lens[b]:
+                continue
+            n = min(chunk, lens[b] - done[b])
+            sel = slice(done[b], done[b] + n)
+            kb, vb = kr[b:b + 1, sel].contiguous(), vr[b:b + 1, sel].contiguous()
+            da.append(kb.to(dev), vb.to(dev), table[b:b + 1], torch.tensor([done[b]], dtype=torch.int32, device=dev),
+                      kc, vc, ks, rope="neox", rope_theta=5e5, pos_host=[done[b]])
+            rk, rv, rs = oracle.append(_np(kb), _np(vb), x["block_table"].numpy()[b:b + 1], [done[b]], rk, rv, rs,
+                                       rope="neox", rope_theta=5e5)
+            done[b] += n
+    torch.cuda.synchronize()
+    assert _pools_equal(_np(kc), rk) and _pools_equal(_np(vc), rv) and _pools_equal(_np(ks), rs)
+    q = x["q"].to(dev)
+    ctx = x["ctx_len"].to(dev)
+    for kw in (dict(mode="full"), dict(mode="fold", window=300, alpha=2.0, beta=-1.0)):
+        side = ks if kw["mode"] == "fold" else None
+        out, lse = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, **kw)
+        torch.cuda.synchronize()
+        ref = oracle.decode(_np(x["q"]), rk, rv, x["block_table"].numpy(), lens, k_side=rs, rope_theta=5e5, **kw)
+        dout = float(np.abs(out.cpu().numpy() - ref["out"]).max())
+        dlse = float(np.abs(lse.cpu().numpy() - ref["lse"]).max())
+        print(f"appended cache {kw}: max|dout|={dout:.3e} max|dlse|={dlse:.3e}", flush=True)
+        assert dout <= 1e-2 and dlse <= 1e-3

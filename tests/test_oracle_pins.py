@@ -494,3 +494,69 @@ def test_block_table_shuffle_invariance():
         a = ref.decode(q, k, v, table, ctx, mode, k_side=ks, **kw)
         bb = ref.decode(q, k2, v2, t2, ctx, mode, k_side=ks2, **kw)
         assert np.array_equal(a["out"], bb["out"]) and np.array_equal(a["lse"], bb["lse"])
+
+
+# ----------------------------------------------------------------------------- cache append
+def test_bf16_rounding_closed_forms():
+    u = 2.0 ** -7                                    # bf16 spacing in [1, 2)
+    cases = {1.0: 1.0, 1 + u / 2: 1.0, 1 + 3 * u / 2: 1 + 2 * u,        # ties go to even
+             1 + u / 2 + 2 ** -30: 1 + u, 1 + u / 2 - 2 ** -30: 1.0,
+             -(1 + 3 * u / 2): -(1 + 2 * u), 3.0 + 2 ** -20: 3.0, 0.0: 0.0,
+             2 ** -100 * (1 + u / 2): 2 ** -100, 255.5: 256.0, 254.5: 254.0}
+    for x, want in cases.items():
+        assert ref.bf16_round(np.array([x]))[0] == want, x
+    # agrees with torch's float32 -> bf16 rounding on float32-representable inputs
+    import torch
+    xs = np.random.default_rng(0).standard_normal(20000).astype(np.float32).astype(np.float64) * 7
+    t = torch.from_numpy(xs.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(ref.bf16_round(xs), t)
+
+
+def test_append_places_tokens_at_their_positions():
+    # Tokens appended at positions pos[b] + i are read back at those logical positions,
+    # the side cache holds the raw key, the rotated cache R(p) k rounded to bf16.
+    rng = np.random.default_rng(3)
+    Hkv, d, theta = 2, 16, 1e4
+    lens = [5, 30]
+    k, v, ks, table = paged([48, 48], Hkv, d, seed=4, side=True, nan_pad=False)
+    kn = rng.standard_normal((2, 7, Hkv, d))
+    vn = rng.standard_normal((2, 7, Hkv, d))
+    kc, vc, ksc = ref.append(kn, vn, table, lens, k, v, ks, rope="neox", rope_theta=theta)
+    for b, L in enumerate(lens):
+        for h in range(Hkv):
+            K, V = logical_rows(kc, vc, table[b], h, 48, d)
+            U, _ = logical_rows(ksc, vc, table[b], h, 48, d)
+            K0, V0 = logical_rows(k, v, table[b], h, 48, d)
+            for i in range(7):
+                p = L + i
+                assert np.array_equal(U[p], kn[b, i, h]) and np.array_equal(V[p], vn[b, i, h])
+                want = ref.bf16_round(np.array(brute.rotate(list(kn[b, i, h]), p, theta)))
+                assert np.array_equal(K[p], want)
+            untouched = [j for j in range(48) if not (L <= j < L + 7)]
+            assert np.array_equal(K[untouched], K0[untouched]) and np.array_equal(V[untouched], V0[untouched])
+    # no rotation: the rotated cache receives the raw key
+    kc2, _, _ = ref.append(kn, vn, table, lens, k, v, None, rope="none")
+    K, _ = logical_rows(kc2, vc, table[1], 0, 48, d)
+    assert np.array_equal(K[30], kn[1, 0, 0])
+
+
+def test_appended_cache_fold_reduces_to_full_attention():
+    # A cache written by append: FOLD with alpha = 1, beta = 0 on (rotated cache, side
+    # cache) equals full attention over a cache whose far keys are the side keys rotated
+    # to the shared position -- the side cache really holds the unrotated keys.
+    rng = np.random.default_rng(8)
+    Hkv, d, theta, L = 1, 16, 1e4, 40
+    k, v, ks, table = paged([L], Hkv, d, seed=9, side=True, nan_pad=False)
+    kn = rng.standard_normal((1, L, Hkv, d))
+    vn = rng.standard_normal((1, L, Hkv, d))
+    kc, vc, ksc = ref.append(kn, vn, table, [0], k, v, ks, rope="neox", rope_theta=theta)
+    q = rng.standard_normal((1, 2, 2, d))
+    W = 9
+    P_v = L - W - 1
+    K, V = logical_rows(kc, vc, table[0], 0, L, d)
+    U, _ = logical_rows(ksc, vc, table[0], 0, L, d)
+    mat = np.array([brute.rotate(list(U[j]), P_v, theta) if j < L - W else K[j] for j in range(L)])
+    k2, v2, t2 = repage(mat, V, d)
+    fold = ref.decode(q, kc, vc, table, [L], "fold", window=W, alpha=1.0, beta=0.0, k_side=ksc, rope_theta=theta)
+    full = ref.decode(q, k2, v2, t2, [L], "full")
+    assert np.allclose(fold["out"], full["out"], atol=1e-12) and np.allclose(fold["lse"], full["lse"], atol=1e-12)
