@@ -86,7 +86,7 @@ def _load():
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          "or python -m draft_attention_amd.build")
+                          "or python draft_attention_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Params)
     vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
@@ -98,6 +98,8 @@ def _load():
     lib.draft_attn_decode.restype = ctypes.c_int
     lib.draft_attn_plan.argtypes = [P, i32p, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), i32p]
     lib.draft_attn_plan.restype = ctypes.c_int
+    lib.draft_attn_merge_draft.argtypes = [P, vp, vp, vp, vp, i32p, vp, vp, vp]
+    lib.draft_attn_merge_draft.restype = ctypes.c_int
     AP = ctypes.POINTER(AppendParams)
     lib.draft_attn_append_params_init.argtypes = [AP]
     lib.draft_attn_append_params_init.restype = None
@@ -313,3 +315,25 @@ def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, *, rop
                                None if k_side is None else k_side.data_ptr(), s)
     if st != OK:
         raise DraftAttnError(st, "draft_attn_append")
+
+
+def merge_draft(q, k_draft, v_draft, ctx_len, out, lse, *, num_blocks, max_blocks_per_seq, num_kv_heads,
+                mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0, n0=1, softmax_scale=None,
+                rope="neox", rope_theta=1e4, ctx_lens=None, stream=None):
+    """Enqueue draft_attn_merge_draft: fold the draft tokens' causal self-attention into
+    (out, lse) from decode() of the same step, in place. k_draft, v_draft: [B, T, Hkv, d] bf16."""
+    import torch
+
+    B, T, Hq, d = q.shape
+    if ctx_lens is None:
+        ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
+    p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=num_kv_heads, head_dim=d,
+                    num_blocks=num_blocks, max_blocks_per_seq=max_blocks_per_seq, mode=mode, window=window,
+                    n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0, softmax_scale=softmax_scale,
+                    rope=rope, rope_theta=rope_theta)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
+    st = lib.draft_attn_merge_draft(ctypes.byref(p), q.data_ptr(), k_draft.data_ptr(), v_draft.data_ptr(),
+                                    ctx_len.data_ptr(), _host_i32(ctx_lens), out.data_ptr(), lse.data_ptr(), s)
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_merge_draft")
+    return out, lse

@@ -1,6 +1,7 @@
 """Compile libdraft_attn.so in-tree for gfx950 with hipcc.
 
-Usage: python -m draft_attention_amd.build  (or __graft_entry__.build()).
+Usage: python draft_attention_amd/build.py  (or __graft_entry__.build()). It does
+not import the package, whose import loads the library this script builds.
 """
 
 from __future__ import annotations
@@ -13,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdraft_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-HIP_SOURCES = [os.path.join(HERE, "csrc", "decode.hip"), os.path.join(HERE, "csrc", "append.hip")]
+HIP_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("decode.hip", "append.hip", "draft.hip")]
 CXX_SOURCES = [os.path.join(HERE, "csrc", "host.cpp")]  # pure C++: built by the host compiler
 
 # Packed fp32 VALU ops are turned off for all device code.
@@ -33,6 +34,8 @@ def _run(cmd, verbose):
         raise RuntimeError(f"{cmd[0]} failed with status {res.returncode}")
     if verbose and out.strip():
         print(out)
+    elif res.returncode == 0 and "error" in out.lower():
+        sys.stderr.write(out + "\n")
 
 
 def build(verbose: bool = False, extra=()) -> str:

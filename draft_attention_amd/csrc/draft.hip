@@ -1,0 +1,136 @@
+// Draft-token self-attention merged into the cache attention, for CDNA4 (gfx950).
+//
+// Within one draft step, draft token t also attends to the step's own draft keys
+// 0..t, which are not in the cache yet. draft_attn_decode returns the cache part
+// as (out, lse); this kernel computes the causal part over the draft keys and
+// merges the two in place: lse <- logaddexp(lse, lse_d) and out <- the matching
+// weighted sum. That is exactly one softmax over the cached visible keys and
+// the draft keys 0..t. In FOLD the draft keys sit at exact positions next to the
+// window, so they join its partition, and the same merge is exact. The logits
+// use the cache call's scale softmax_scale * s(n), with n the cached visible
+// count ("SharpDraft: Accelerating Long-Context Speculative Decoding with
+// Cardinality-Aware Query Scaling", Abstract, scales by the visible keys; the
+// few draft keys do not change n here).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "host.h"
+#include "plan.h"
+
+namespace da {
+
+struct MergeArgs {
+  const __bf16* q;   // [B][T][Hq][D]
+  const __bf16* kd;  // [B][T][Hkv][D], rotated at the draft positions
+  const __bf16* vd;  // [B][T][Hkv][D]
+  const int32_t* ctx_len;
+  float* out;        // [B][T][Hq][D], in place
+  float* lse;        // [B][T][Hq], in place
+  int32_t B, T, Hq, Hkv, G, mode, W, S, n0;
+  float kappa, scale;
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// One wave per (sequence, draft token, query head); lane l owns channels
+// l*CPL .. l*CPL + CPL - 1.
+template <int D>
+__global__ __launch_bounds__(64) void merge_draft_kernel(const MergeArgs a) {
+  constexpr int CPL = D / 64;
+  const int lane = threadIdx.x;
+  int64_t r = blockIdx.x;
+  const int32_t h = (int32_t)(r % a.Hq);
+  r /= a.Hq;
+  const int32_t t = (int32_t)(r % a.T);
+  const int32_t b = (int32_t)(r / a.T);
+  const int32_t kvh = h / a.G;
+  const int32_t n = visible_count(a.ctx_len[b], a.mode, a.W, a.S);
+  const double sn = 1.0 + (double)a.kappa * log((double)(n > a.n0 ? n : a.n0) / (double)a.n0);
+  const float c = (float)((double)a.scale * sn);
+
+  const int64_t qrow = ((int64_t)b * a.T + t) * a.Hq + h;
+  float qv[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) qv[j] = (float)a.q[qrow * D + lane * CPL + j];
+
+  // Logits of draft keys 0..t as wave-reduced dot products: one pass for the
+  // maximum, a second (recomputing them) for the sums.
+  auto logit = [&](int32_t j) {
+    const __bf16* kr = a.kd + (((int64_t)b * a.T + j) * a.Hkv + kvh) * D + lane * CPL;
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) part += qv[e] * (float)kr[e];
+    return c * wave_sum(part);
+  };
+  float m = -INFINITY;
+  for (int32_t j = 0; j <= t; ++j) m = fmaxf(m, logit(j));
+  float z = 0.f, od[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) od[e] = 0.f;
+  for (int32_t j = 0; j <= t; ++j) {
+    const float pj = expf(logit(j) - m);
+    z += pj;
+    const __bf16* vr = a.vd + (((int64_t)b * a.T + j) * a.Hkv + kvh) * D + lane * CPL;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) od[e] += pj * (float)vr[e];
+  }
+  const float lse_d = m + logf(z);
+  const float lse_c = a.lse[qrow];
+  const float top = fmaxf(lse_c, lse_d);
+  const float wc = expf(lse_c - top), wd = expf(lse_d - top);
+  const float den = wc + wd;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    float* o = a.out + qrow * D + lane * CPL + e;
+    const float oc = wc > 0.f ? *o : 0.f;
+    *o = (wc * oc + wd * od[e] / z) / den;
+  }
+  if (lane == 0) a.lse[qrow] = top + logf(den);
+}
+
+}  // namespace da
+
+extern "C" int draft_attn_merge_draft(const draft_attn_params* p, const void* q, const void* k_draft,
+                                      const void* v_draft, const int32_t* ctx_len_dev, const int32_t* ctx_len_host,
+                                      float* out, float* lse, void* stream) {
+  using namespace da;
+  Prepared pr;
+  const int st = prepare(p, ctx_len_host, &pr);
+  if (st != DRAFT_ATTN_OK) return st;
+  if (p->num_seqs == 0) return DRAFT_ATTN_OK;
+  if (p->num_draft_tokens > DRAFT_ATTN_MAX_ROWS) return DRAFT_ATTN_ENOTSUP;
+  if (!q || !k_draft || !v_draft || !ctx_len_dev || !out || !lse) return DRAFT_ATTN_EINVAL;
+  auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
+  if (mis(q, 16) || mis(k_draft, 16) || mis(v_draft, 16) || mis(out, 8) || mis(lse, 4) || mis(ctx_len_dev, 4))
+    return DRAFT_ATTN_EINVAL;
+  MergeArgs a;
+  a.q = (const __bf16*)q;
+  a.kd = (const __bf16*)k_draft;
+  a.vd = (const __bf16*)v_draft;
+  a.ctx_len = ctx_len_dev;
+  a.out = out;
+  a.lse = lse;
+  a.B = p->num_seqs;
+  a.T = p->num_draft_tokens;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = pr.G;
+  a.mode = p->mode;
+  a.W = p->window;
+  a.S = p->n_sink;
+  a.n0 = p->n0;
+  a.kappa = p->kappa;
+  a.scale = p->softmax_scale;
+  const uint32_t grid = (uint32_t)((int64_t)a.B * a.T * a.Hq);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (p->head_dim == 64) merge_draft_kernel<64><<<grid, 64, 0, s>>>(a);
+  else merge_draft_kernel<128><<<grid, 64, 0, s>>>(a);
+  if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
+  return DRAFT_ATTN_OK;
+}

@@ -185,6 +185,25 @@ int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int
                     int64_t capacity, int64_t* n_items, int32_t* chunk_keys);
 
 /* ---------------------------------------------------------------------------
+ * Draft-token self-attention, merged into a draft_attn_decode result in place.
+ * Within one draft step, draft token t also attends to the step's own draft keys
+ * 0..t, which are not in the cache yet. Given the cache attention (out, lse) of
+ * the same step and params, this computes, per (b, t, h),
+ *   lse_d = ln sum_{j<=t} e^{c <q, kd_j>},  out_d = sum_{j<=t} e^{c <q, kd_j> - lse_d} vd_j
+ * and replaces (out, lse) by the merge of the two: lse <- logaddexp(lse, lse_d),
+ * out <- e^{lse_old - lse} out + e^{lse_d - lse} out_d. The result is one softmax
+ * over the cached visible keys and draft keys 0..t; in FOLD the draft keys join
+ * the local window (they sit at exact positions next to it). c is the cache
+ * call's scale softmax_scale * s(n), n the cached visible count (a reading: the
+ * pages do not say whether the draft's own keys count).
+ * q: bf16 [B][T][Hq][d] (the same queries as the decode call); k_draft (already
+ * rotated at positions L_b + t) and v_draft: bf16 [B][T][Hkv][d]; out, lse: as
+ * written by draft_attn_decode. p, ctx_len_dev and ctx_len_host: as for that call. */
+int draft_attn_merge_draft(const draft_attn_params* p, const void* q, const void* k_draft, const void* v_draft,
+                           const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out, float* lse,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * KV append with FOLD side-cache bookkeeping. For token i < num_new of sequence
  * b, at position p = pos[b] + i, in block block_table[b][p / 16] and slot p % 16:
  *   k_cache <- R(p) k_new[b][i]  rounded to bf16 (to nearest, ties to even) from

@@ -29,6 +29,7 @@ from .reference import (  # noqa: F401
     append,
     bf16_round,
     decode,
+    decode_with_draft,
     index_sets,
     visible_count,
     query_scale,

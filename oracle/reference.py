@@ -263,3 +263,58 @@ def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, rope: 
                     ks[blk, h, :, slot, :] = raw.reshape(d // 8, 8)
                 vc[blk, h, :, slot] = v_new[b, i, h]
     return kc, vc, ks
+
+
+# ----------------------------------------------------------------------------- draft tokens
+def decode_with_draft(q, k_cache, v_cache, block_table, ctx_len, mode: str, k_draft, v_draft, *,
+                      window: int = 0, n_sink: int = 0, alpha: float = 1.0, beta: float = 0.0,
+                      kappa: float = 0.0, n0: int = 1, softmax_scale: float | None = None,
+                      rope: str = "neox", rope_theta: float = 1e4, k_side=None):
+    """Cache attention plus causal attention among the draft tokens, as one softmax.
+
+    Draft token t of sequence b also attends to the step's own draft keys
+    k_draft[b, 0..t] (already rotated at their positions L_b + t'), which are not
+    in the cache yet. They sit at exact positions next to the window, so for FOLD
+    they join the local partition. Reading (no page states it): their logits use
+    the same scale c = softmax_scale * s(n) as the cached keys, with n the
+    cached visible count. q: [B, T, Hq, d]; k_draft, v_draft: [B, T, Hkv, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kd = np.asarray(k_draft, dtype=np.float64)
+    vd = np.asarray(v_draft, dtype=np.float64)
+    B, T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = np.zeros((B, T, Hq, d))
+    lse = np.zeros((B, T, Hq))
+    for b in range(B):
+        L = int(ctx_len[b])
+        main, far = index_sets(L, mode, window, n_sink)
+        c = scale * query_scale(int(main.size + far.size), kappa, n0)
+        row = block_table[b]
+        for g in range(Hkv):
+            K = gather_keys(k_cache, row, main, g)
+            V = gather_values(v_cache, row, main, g)
+            if mode == "fold":
+                U = gather_keys(k_side, row, far, g)
+                Vf = gather_values(v_cache, row, far, g)
+            for t in range(T):
+                Q = q[b, t, g * G:(g + 1) * G, :]                       # [G, d]
+                Km = np.concatenate([K, kd[b, :t + 1, g, :]])           # main keys + draft keys <= t
+                Vm = np.concatenate([V, vd[b, :t + 1, g, :]])
+                logits = c * (Q @ Km.T)
+                if mode == "fold":
+                    Qf = rope_rotate(Q, -(L - int(window) - 1), rope_theta) if rope == "neox" else Q
+                    phi = c * (Qf @ U.T)
+                    lse_L, lse_F, lse_Fa = _logsumexp(logits), _logsumexp(phi), _logsumexp(alpha * phi)
+                    tot = np.logaddexp(lse_L, beta + lse_F)
+                    with np.errstate(invalid="ignore"):
+                        w_far = np.exp(beta + lse_F - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])
+                    o = np.exp(logits - tot[:, None]) @ Vm + (w_far @ Vf if far.size else 0.0)
+                else:
+                    tot = _logsumexp(logits)
+                    o = np.exp(logits - tot[:, None]) @ Vm
+                out[b, t, g * G:(g + 1) * G] = o
+                lse[b, t, g * G:(g + 1) * G] = tot
+    return dict(out=out, lse=lse)

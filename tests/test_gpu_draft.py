@@ -1,0 +1,47 @@
+"""GPU parity of draft-token self-attention merged into the cache attention
+(draft_attn_decode followed by draft_attn_merge_draft) against the oracle's
+single softmax over cached visible keys and draft keys 0..t."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mode="full"),
+    dict(mode="window", window=500, n_sink=4),
+    dict(mode="fold", window=700, alpha=2.0, beta=-1.0),
+    dict(mode="full", kappa=0.2, n0=256),
+    dict(mode="fold", window=300, alpha=4.0, beta=0.5, kappa=0.1, n0=64, rope="none"),
+], ids=["full", "window", "fold", "full-kappa", "fold-kappa-nope"])
+@pytest.mark.parametrize("d,T,G", [(128, 4, 4), (64, 8, 2), (128, 1, 8)])
+def test_decode_then_merge_draft(kw, d, T, G):
+    import draft_attention_amd as da
+    dev = torch.device("cuda:0")
+    lens = [0, 5, 3000, 1234]
+    Hkv = 2
+    x = synth.make_inputs(ctx_lens=lens, T=T, Hq=G * Hkv, Hkv=Hkv, d=d, seed=61, fold=True)
+    g = torch.Generator().manual_seed(62)
+    kd = (torch.randn((4, T, Hkv, d), generator=g) * 2).to(torch.bfloat16)
+    vd = torch.randn((4, T, Hkv, d), generator=g).to(torch.bfloat16)
+    q, kc, vc, ks = (x[k].to(dev) for k in ("q", "k_cache", "v_cache", "k_side"))
+    table, ctx = x["block_table"].to(dev), x["ctx_len"].to(dev)
+    side = ks if kw["mode"] == "fold" else None
+    out, lse = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, **kw)
+    da.merge_draft(q, kd.to(dev), vd.to(dev), ctx, out, lse, num_blocks=kc.shape[0],
+                   max_blocks_per_seq=table.shape[1], num_kv_heads=Hkv, ctx_lens=lens, rope_theta=5e5, **kw)
+    torch.cuda.synchronize()
+    n = {k: (v.float().numpy() if torch.is_tensor(v) and v.is_floating_point() else v) for k, v in x.items()}
+    ref = oracle.decode_with_draft(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), lens, kw["mode"],
+                                   kd.float().numpy(), vd.float().numpy(), k_side=n["k_side"], rope_theta=5e5,
+                                   **{k: v for k, v in kw.items() if k != "mode"})
+    dout = float(np.abs(out.cpu().numpy() - ref["out"]).max())
+    dlse = float(np.abs(lse.cpu().numpy() - ref["lse"]).max())
+    print(f"merge_draft {kw} d={d} T={T} G={G}: max|dout|={dout:.3e} max|dlse|={dlse:.3e}", flush=True)
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert dout <= 1e-2 and dlse <= 1e-3

@@ -560,3 +560,65 @@ def test_appended_cache_fold_reduces_to_full_attention():
     fold = ref.decode(q, kc, vc, table, [L], "fold", window=W, alpha=1.0, beta=0.0, k_side=ksc, rope_theta=theta)
     full = ref.decode(q, k2, v2, t2, [L], "full")
     assert np.allclose(fold["out"], full["out"], atol=1e-12) and np.allclose(fold["lse"], full["lse"], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- draft tokens
+def _draft_inputs(ctx, T, Hkv, G, d, seed):
+    k, v, ks, table = paged(ctx, Hkv, d, seed=seed, side=True, nan_pad=False, spare=4)
+    rng = np.random.default_rng(seed + 1)
+    q = rng.standard_normal((len(ctx), T, Hkv * G, d))
+    kd = rng.standard_normal((len(ctx), T, Hkv, d))
+    vd = rng.standard_normal((len(ctx), T, Hkv, d))
+    return k, v, ks, table, q, kd, vd
+
+
+def test_draft_tokens_equal_decode_over_the_extended_cache():
+    # Token t's result equals plain decode over the cache with draft keys 0..t
+    # appended as cache entries (kappa = 0, so the visible count does not matter).
+    ctx, T, Hkv, G, d = [37, 13], 3, 2, 2, 8        # draft positions L..L+2 stay inside allocated blocks
+    k, v, ks, table, q, kd, vd = _draft_inputs(ctx, T, Hkv, G, d, seed=51)
+    assert all(table[b, (L + T - 1) // BLOCK] >= 0 for b, L in enumerate(ctx))
+    for mode, kw in (("full", {}), ("window", dict(window=9, n_sink=2)), ("fold", dict(window=9, alpha=2.0, beta=-1.0))):
+        res = ref.decode_with_draft(q, k, v, table, ctx, mode, kd, vd, k_side=ks, rope_theta=100.0, **kw)
+        for b, L in enumerate(ctx):
+            for t in range(T):
+                k2, v2, ks2 = k.copy(), v.copy(), ks.copy()
+                for tt in range(t + 1):         # write draft key tt at position L + tt
+                    p = L + tt
+                    for h in range(Hkv):
+                        put_key(k2, table[b, p // BLOCK], h, p % BLOCK, kd[b, tt, h])
+                        put_key(ks2, table[b, p // BLOCK], h, p % BLOCK, np.full(d, np.nan))
+                        v2[table[b, p // BLOCK], h, :, p % BLOCK] = vd[b, tt, h]
+                # the window / local window grows with the appended keys: W + t + 1
+                kw2 = dict(kw)
+                if "window" in kw2:
+                    kw2["window"] = kw["window"] + t + 1
+                r2 = ref.decode(q[b:b + 1, t:t + 1], k2, v2, table[b:b + 1], [L + t + 1], mode, k_side=ks2,
+                                rope_theta=100.0, **kw2)
+                # (FOLD's shared far position is unchanged: L + t + 1 - (W + t + 1) - 1 = L - W - 1)
+                assert np.allclose(res["out"][b, t], r2["out"][0, 0], atol=1e-12), (mode, b, t)
+                assert np.allclose(res["lse"][b, t], r2["lse"][0, 0], atol=1e-12), (mode, b, t)
+
+
+def test_draft_tokens_on_an_empty_cache_are_causal_attention():
+    T, Hkv, G, d = 4, 1, 2, 8
+    k, v, ks, table, q, kd, vd = _draft_inputs([0], T, Hkv, G, d, seed=52)
+    res = ref.decode_with_draft(q, k, v, table, [0], "full", kd, vd, softmax_scale=0.5)
+    for t in range(T):
+        for h in range(G):
+            logits = [0.5 * q[0, t, h] @ kd[0, j, 0] for j in range(t + 1)]
+            m = max(logits)
+            z = sum(math.exp(x - m) for x in logits)
+            want = sum(math.exp(x - m) / z * vd[0, j, 0] for j, x in enumerate(logits))
+            assert np.allclose(res["out"][0, t, h], want, atol=1e-13)
+            assert abs(res["lse"][0, t, h] - (m + math.log(z))) < 1e-13
+
+
+def test_draft_tokens_keep_the_cached_visible_count_for_kappa():
+    # Reading: the query scale uses the cached visible count n, not n + t + 1.
+    ctx, T, Hkv, G, d = [50], 2, 1, 1, 8
+    k, v, ks, table, q, kd, vd = _draft_inputs(ctx, T, Hkv, G, d, seed=53)
+    s = ref.query_scale(50, 0.4, 4)
+    a = ref.decode_with_draft(q, k, v, table, ctx, "full", kd, vd, kappa=0.4, n0=4)
+    b_ = ref.decode_with_draft(q * s, k, v, table, ctx, "full", kd, vd)
+    assert np.allclose(a["out"], b_["out"], atol=1e-13) and np.allclose(a["lse"], b_["lse"], atol=1e-13)
