@@ -100,6 +100,11 @@ def _load():
     lib.draft_attn_plan.restype = ctypes.c_int
     lib.draft_attn_merge_draft.argtypes = [P, vp, vp, vp, vp, i32p, vp, vp, vp]
     lib.draft_attn_merge_draft.restype = ctypes.c_int
+    lib.draft_attn_ring_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p, i32p]
+    lib.draft_attn_ring_size.restype = ctypes.c_int
+    lib.draft_attn_ring_table.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p,
+                                          ctypes.c_int32, i32p, ctypes.c_int32, i32p, ctypes.c_int32]
+    lib.draft_attn_ring_table.restype = ctypes.c_int
     AP = ctypes.POINTER(AppendParams)
     lib.draft_attn_append_params_init.argtypes = [AP]
     lib.draft_attn_append_params_init.restype = None
@@ -337,3 +342,24 @@ def merge_draft(q, k_draft, v_draft, ctx_len, out, lse, *, num_blocks, max_block
     if st != OK:
         raise DraftAttnError(st, "draft_attn_merge_draft")
     return out, lse
+
+
+def ring_size(window, n_sink, max_new):
+    """(sink_blocks, ring_len) of the compact window-mode ring for these sizes."""
+    sb, rl = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib.draft_attn_ring_size(int(window), int(n_sink), int(max_new), ctypes.byref(sb), ctypes.byref(rl))
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_ring_size")
+    return int(sb.value), int(rl.value)
+
+
+def ring_table(length, max_new, window, n_sink, sink_phys, ring_phys, max_blocks_per_seq):
+    """Block-table row (list of ints) of a ring-buffer sequence; see draft_attn_ring_table."""
+    row = (ctypes.c_int32 * int(max_blocks_per_seq))()
+    sp = (ctypes.c_int32 * max(len(sink_phys), 1))(*sink_phys)
+    rp = (ctypes.c_int32 * max(len(ring_phys), 1))(*ring_phys)
+    st = lib.draft_attn_ring_table(int(length), int(max_new), int(window), int(n_sink), sp, len(sink_phys), rp,
+                                   len(ring_phys), row, int(max_blocks_per_seq))
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_ring_table")
+    return list(row)

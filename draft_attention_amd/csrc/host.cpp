@@ -225,6 +225,38 @@ int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int
   return DRAFT_ATTN_OK;
 }
 
+int draft_attn_ring_size(int32_t window, int32_t n_sink, int32_t max_new, int32_t* sink_blocks,
+                         int32_t* ring_len) {
+  if (window < 0 || n_sink < 0 || max_new < 0 || !sink_blocks || !ring_len) return DRAFT_ATTN_EINVAL;
+  if (window > (1 << 30) || n_sink > (1 << 30) || max_new > (1 << 30)) return DRAFT_ATTN_EINVAL;
+  *sink_blocks = (n_sink + 15) / 16;
+  *ring_len = (window + 15) / 16 + 1 + (max_new + 15) / 16;
+  return DRAFT_ATTN_OK;
+}
+
+int draft_attn_ring_table(int32_t length, int32_t max_new, int32_t window, int32_t n_sink,
+                          const int32_t* sink_phys, int32_t sink_blocks, const int32_t* ring_phys,
+                          int32_t ring_len, int32_t* table_row, int32_t max_blocks_per_seq) {
+  int32_t need_sinks = 0, need_ring = 0;
+  if (draft_attn_ring_size(window, n_sink, max_new, &need_sinks, &need_ring) != DRAFT_ATTN_OK) return DRAFT_ATTN_EINVAL;
+  if (length < 0 || !table_row || max_blocks_per_seq < 1) return DRAFT_ATTN_EINVAL;
+  if (sink_blocks < need_sinks || ring_len < need_ring) return DRAFT_ATTN_EINVAL;
+  if ((sink_blocks > 0 && !sink_phys) || !ring_phys) return DRAFT_ATTN_EINVAL;
+  const int64_t end = (int64_t)length + max_new;  // one past the last position touched
+  if (end > (int64_t)max_blocks_per_seq * 16) return DRAFT_ATTN_EINVAL;
+  for (int32_t j = 0; j < max_blocks_per_seq; ++j) table_row[j] = -1;
+  if (end == 0) return DRAFT_ATTN_OK;
+  // Blocks touched: the sinks, and the window of the read through the last append.
+  const int64_t s_end = n_sink < length ? n_sink : length;
+  const int64_t w0 = length - window > 0 ? length - window : 0;
+  for (int64_t j = 0; j < (s_end + 15) / 16; ++j)
+    table_row[j] = j < sink_blocks ? sink_phys[j] : ring_phys[(j - sink_blocks) % ring_len];
+  if (end > w0)
+    for (int64_t j = w0 / 16; j <= (end - 1) / 16; ++j)
+      table_row[j] = j < sink_blocks ? sink_phys[j] : ring_phys[(j - sink_blocks) % ring_len];
+  return DRAFT_ATTN_OK;
+}
+
 const char* draft_attn_strerror(int status) {
   switch (status) {
     case DRAFT_ATTN_OK: return "ok";

@@ -241,6 +241,33 @@ int draft_attn_append(const draft_attn_append_params* p, const void* k_new, cons
                       const int32_t* block_table, const int32_t* pos_dev, const int32_t* pos_host,
                       void* k_cache, void* v_cache, void* k_side, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Ring-buffer draft cache for WINDOW mode. A window step reads only the sinks
+ * [0, n_sink) and the recent window [L - W, L), so a sequence needs only
+ * sink_blocks = ceil(n_sink / 16) fixed blocks plus a ring of ring_len blocks
+ * that the recent window cycles through; the rest of the draft KV is never read
+ * and need not be kept ["Windowed-MTP: Removing the Full-Context Draft-KV Tax
+ * at Million-Token Context", Abstract: unread draft KV reclaimed by a compact
+ * ring buffer]. Logical block j maps to sink_phys[j] for j < sink_blocks and to
+ * ring_phys[(j - sink_blocks) % ring_len] otherwise.
+ *
+ * draft_attn_ring_size: the smallest sink_blocks and ring_len for a window W,
+ * n_sink sinks and appends of up to max_new tokens between two window reads
+ * (ring_len = ceil(W / 16) + 1 + ceil(max_new / 16)).
+ *
+ * draft_attn_ring_table: fill the block-table row (max_blocks_per_seq entries)
+ * of a sequence of current length `length` that is about to be read in WINDOW
+ * mode and then receive up to max_new appended tokens: entries of the blocks the
+ * read or the appends touch get their physical block, every other entry -1.
+ * Returns DRAFT_ATTN_EINVAL when ring_len or sink_blocks is smaller than
+ * draft_attn_ring_size reports or a touched block lies past max_blocks_per_seq.
+ * Host-only; the decode and append kernels are unchanged. */
+int draft_attn_ring_size(int32_t window, int32_t n_sink, int32_t max_new, int32_t* sink_blocks,
+                         int32_t* ring_len);
+int draft_attn_ring_table(int32_t length, int32_t max_new, int32_t window, int32_t n_sink,
+                          const int32_t* sink_phys, int32_t sink_blocks, const int32_t* ring_phys,
+                          int32_t ring_len, int32_t* table_row, int32_t max_blocks_per_seq);
+
 /* Static description of a status code. */
 const char* draft_attn_strerror(int status);
 

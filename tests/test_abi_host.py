@@ -288,3 +288,28 @@ def test_host_logic_under_sanitizers(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "ok" in res.stdout
+
+
+# ----------------------------------------------------------------------------- ring buffer
+def test_ring_size_and_table_cover_exactly_the_touched_blocks():
+    rnd = random.Random(5)
+    for _ in range(300):
+        W, S, n_new = rnd.choice([0, 1, 16, 100, 256]), rnd.choice([0, 1, 4, 16, 20]), rnd.choice([0, 1, 7, 40])
+        sb, rl = da().ring_size(W, S, n_new)
+        assert sb == -(-S // 16) and rl == -(-W // 16) + 1 + -(-n_new // 16)
+        L = rnd.randint(0, 3000)
+        MB = (L + n_new + 15) // 16 + 1
+        sinks = [1000 + i for i in range(sb)]
+        ring = [2000 + i for i in range(rl)]
+        row = da().ring_table(L, n_new, W, S, sinks, ring, MB)
+        main, _ = oracle.index_sets(L, "window", W, S)
+        touched = set(int(j) // 16 for j in main) | set(p // 16 for p in range(L, L + n_new))
+        assert {j for j, x in enumerate(row) if x >= 0} == touched
+        phys = [row[j] for j in sorted(touched)]
+        assert len(set(phys)) == len(phys), "two touched blocks share a physical block"
+        for j in touched:
+            assert row[j] == (sinks[j] if j < sb else ring[(j - sb) % rl])
+    # rings smaller than the minimum are refused
+    sb, rl = da().ring_size(100, 4, 7)
+    with pytest.raises(da().DraftAttnError):
+        da().ring_table(500, 7, 100, 4, [0] * sb, list(range(rl - 1)), 64)
