@@ -16,11 +16,21 @@ reductions that the pages state in words:
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
 
 from oracle import brute, reference as ref
+
+# tests/test_oracle_mutations.py runs this file against deliberately broken
+# copies of oracle/reference.py (named by ORACLE_REFERENCE_PATH) and expects it
+# to fail for each of them.
+if os.environ.get("ORACLE_REFERENCE_PATH"):
+    import importlib.util
+    _spec = importlib.util.spec_from_file_location("oracle_reference_mutant", os.environ["ORACLE_REFERENCE_PATH"])
+    ref = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(ref)
 
 BLOCK = 16
 
