@@ -22,6 +22,8 @@ MAX_ROWS = 32
 ABI_VERSION = 1
 _MODES = {"full": FULL, "window": WINDOW, "fold": FOLD}
 _ROPES = {"neox": ROPE_NEOX, "none": ROPE_NONE}
+FOLD_B, FOLD_JOINT, FOLD_VIRTUAL = 0, 1, 2
+_FOLD_VARIANTS = {"B": FOLD_B, "A": FOLD_JOINT, "B'": FOLD_VIRTUAL}
 
 
 class Params(ctypes.Structure):
@@ -50,7 +52,7 @@ class Params(ctypes.Structure):
         ("debug_visit_stride", ctypes.c_int64),
         ("prof_events", ctypes.c_void_p * 2),
         ("split_keys", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("fold_variant", ctypes.c_int32),
     ]
 
 
@@ -131,7 +133,7 @@ def strerror(status: int) -> str:
 def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks,
                 max_blocks_per_seq, mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0,
                 n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, split_keys=0,
-                debug_visit=0, debug_visit_stride=0, prof_events=None) -> Params:
+                debug_visit=0, debug_visit_stride=0, prof_events=None, fold_variant="B") -> Params:
     p = Params()
     lib.draft_attn_params_init(ctypes.byref(p))
     p.num_seqs = int(num_seqs)
@@ -154,6 +156,7 @@ def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_d
     p.rope = _ROPES[rope] if isinstance(rope, str) else int(rope)
     p.rope_theta = float(rope_theta)
     p.split_keys = int(split_keys)
+    p.fold_variant = _FOLD_VARIANTS[fold_variant] if isinstance(fold_variant, str) else int(fold_variant)
     p.debug_visit = int(debug_visit) or None
     p.debug_visit_stride = int(debug_visit_stride)
     if prof_events is not None:
@@ -215,7 +218,7 @@ class PreparedDecode:
 def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
             beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
             ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
-            debug_visit=None) -> PreparedDecode:
+            debug_visit=None, fold_variant="B") -> PreparedDecode:
     """Marshal the arguments of decode() once (same meaning as there)."""
     import torch
 
@@ -230,7 +233,8 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
                     num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
                     window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
                     softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
-                    split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride)
+                    split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
+                    fold_variant=fold_variant)
     dev = q.device
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
@@ -251,7 +255,7 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
 def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
            beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
            ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
-           debug_visit=None, prof_events=None):
+           debug_visit=None, prof_events=None, fold_variant="B"):
     """Enqueue draft_attn_decode on the current (or given) stream; returns (out, lse).
 
     q bf16 [B,T,Hq,d]; k_cache / k_side bf16 [NB,Hkv,d/8,16,8]; v_cache bf16 [NB,Hkv,d,16];
@@ -273,7 +277,7 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
                     window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
                     softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                     split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
-                    prof_events=prof_events)
+                    prof_events=prof_events, fold_variant=fold_variant)
     dev = q.device
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)

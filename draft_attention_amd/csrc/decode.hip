@@ -71,7 +71,7 @@ struct Pass2Args {
   float* out;
   float* lse;
   int32_t B, T, Hq, Hkv, G, R, rows_pad;
-  int32_t mode, W, S, C, total_items;
+  int32_t mode, W, S, C, total_items, fold_variant;
   float alpha, beta;
 };
 
@@ -675,8 +675,17 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   __syncthreads();
 
   // Final combine: thread c < D owns output channel c.
+  // log2 weights of the partitions. The far memory weighs e^beta Z_F (default),
+  // e^beta Z_Fa (joint softmax) or e^beta Z_Fa^(1/alpha) (one virtual key); in
+  // the log2 domain Z_F = 2^MF ZF and Z_Fa = 2^(alpha MF) ZFa.
   const float lwL = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
-  const float lwF = ZF > 0.f ? a.beta * kLog2e + MF + log2f(ZF) : -INFINITY;
+  float lwF = -INFINITY;
+  if (ZF > 0.f) {
+    const float far_log2 = a.fold_variant == DRAFT_ATTN_FOLD_JOINT     ? alpha * MF + log2f(ZFa)
+                           : a.fold_variant == DRAFT_ATTN_FOLD_VIRTUAL ? MF + log2f(ZFa) / alpha
+                                                                       : MF + log2f(ZF);
+    lwF = a.beta * kLog2e + far_log2;
+  }
   const float top = fmaxf(lwL, lwF);
   const int32_t t = row / a.G;
   const int32_t head = kvh * a.G + (row - t * a.G);
@@ -795,6 +804,7 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a2.total_items = a1.total_items;
   a2.alpha = p->alpha;
   a2.beta = p->beta;
+  a2.fold_variant = p->fold_variant;
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();  // clear a stale error so the check below reports ours

@@ -81,7 +81,7 @@ bool finite_f(double x) { return isfinite(x) != 0; }
 int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* out) {
   if (!p || !out) return DRAFT_ATTN_EINVAL;
   if (p->struct_size != sizeof(draft_attn_params)) return DRAFT_ATTN_EINVAL;
-  if (p->reserved != 0) return DRAFT_ATTN_EINVAL;
+  if (p->fold_variant < DRAFT_ATTN_FOLD_B || p->fold_variant > DRAFT_ATTN_FOLD_VIRTUAL) return DRAFT_ATTN_EINVAL;
   const int32_t B = p->num_seqs, T = p->num_draft_tokens, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
   if (B < 0 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DRAFT_ATTN_EINVAL;
   if (p->block_size != kBlock) return DRAFT_ATTN_EINVAL;

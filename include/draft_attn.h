@@ -51,6 +51,14 @@
  *    weight against the window is e^beta Z_F / Z_L [FOLD, abstract]. alpha = 1,
  *    beta = 0 is one softmax over Loc U Far.
  * 6. An empty visible set gives out = 0 and lse = -inf.
+ * 7. fold_variant selects other readings of FOLD's alpha/beta (same Z_L, Z_F, Z_Fa):
+ *    DRAFT_ATTN_FOLD_B       (0, default) as in 5.
+ *    DRAFT_ATTN_FOLD_JOINT   (1) one softmax with far logits alpha phi_j + beta:
+ *                            lse = ln(Z_L + e^beta Z_Fa); alpha also scales the far total.
+ *    DRAFT_ATTN_FOLD_VIRTUAL (2) the far memory is one virtual key with logit
+ *                            beta + ln(Z_Fa)/alpha and value sum_Far (e^{alpha phi_j}/Z_Fa) v_j:
+ *                            lse = ln(Z_L + e^beta Z_Fa^(1/alpha)).
+ *    All three are one softmax over Loc U Far at alpha = 1, beta = 0.
  *
  * ---------------------------------------------------------------------------
  * Layouts. All tensors are device memory owned by the caller; the library
@@ -111,6 +119,11 @@ extern "C" {
 #define DRAFT_ATTN_ROPE_NEOX 0
 #define DRAFT_ATTN_ROPE_NONE 1
 
+/* FOLD parameterisations (fold_variant) */
+#define DRAFT_ATTN_FOLD_B 0
+#define DRAFT_ATTN_FOLD_JOINT 1
+#define DRAFT_ATTN_FOLD_VIRTUAL 2
+
 /* status codes */
 #define DRAFT_ATTN_OK 0
 #define DRAFT_ATTN_EINVAL (-1)   /* bad argument, shape, pointer or alignment */
@@ -151,7 +164,7 @@ typedef struct draft_attn_params {
                                   before and just after the streaming pass; NULL: off */
   int32_t split_keys;          /* keys per work item: 0 = chosen by the library, else a
                                   multiple of 32 in [32, 65536] */
-  int32_t reserved;            /* must be 0 */
+  int32_t fold_variant;        /* DRAFT_ATTN_FOLD_B (default), _JOINT or _VIRTUAL */
 } draft_attn_params;
 
 /* Fill *p with defaults: FULL mode, block_size 16, alpha 1, beta 0, kappa 0,

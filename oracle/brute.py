@@ -67,7 +67,7 @@ def _dot(a, b):
 def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int = 0,
            n_sink: int = 0, alpha: float = 1.0, beta: float = 0.0, kappa: float = 0.0,
            n0: int = 1, softmax_scale=None, rope: str = "neox", rope_theta: float = 1e4,
-           k_side=None):
+           k_side=None, fold_variant: str = "B"):
     """Return (out, lse, weights): nested lists out[b][t][h][i], lse[b][t][h] and
     weights[b][t][h] = {key: (partition, weight)} with partition 'main' or 'far'."""
     B, T, Hq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -114,7 +114,12 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int 
                         mF = max(phi.values())
                         zF = sum(math.exp(v - mF) for v in phi.values())
                         zFa = sum(math.exp(alpha * (v - mF)) for v in phi.values())
-                        log_far_mass = beta + mF + math.log(zF)
+                        if fold_variant == "A":      # joint softmax, far logits alpha*phi + beta
+                            log_far_mass = beta + alpha * mF + math.log(zFa)
+                        elif fold_variant == "B'":   # one virtual key, logit beta + ln(Z_Fa)/alpha
+                            log_far_mass = beta + mF + math.log(zFa) / alpha
+                        else:
+                            log_far_mass = beta + mF + math.log(zF)
                         parts.append(log_far_mass)
                     top = max(parts)
                     log_den = top + math.log(sum(math.exp(p - top) for p in parts))

@@ -58,6 +58,13 @@ What is computed, per sequence b, draft token t and query head h:
     weight relative to the window is e^beta Z_F / Z_L. With alpha = 1 and
     beta = 0 this is one softmax over Loc U Far.
  6. An empty visible set gives out = 0 and lse = -inf.
+ 7. Alternative FOLD parameterisations (``fold_variant``), same definitions of
+    Z_L, Z_F, Z_Fa:
+      "A"  joint softmax with far logits alpha phi_j + beta:
+           lse = ln(Z_L + e^beta Z_Fa); far key j weighs e^(alpha phi_j + beta - lse)
+      "B'" far memory as one virtual key with logit beta + ln(Z_Fa)/alpha and value
+           sum_Far (e^{alpha phi_j} / Z_Fa) v_j: lse = ln(Z_L + e^beta Z_Fa^(1/alpha))
+    All three reduce to one softmax over Loc U Far at alpha = 1, beta = 0.
 """
 
 from __future__ import annotations
@@ -144,7 +151,8 @@ def _logsumexp(x: np.ndarray) -> np.ndarray:
 def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int = 0,
            n_sink: int = 0, alpha: float = 1.0, beta: float = 0.0, kappa: float = 0.0,
            n0: int = 1, softmax_scale: float | None = None, rope: str = "neox",
-           rope_theta: float = 1e4, k_side=None, pairs=None, details: bool = False):
+           rope_theta: float = 1e4, k_side=None, pairs=None, details: bool = False,
+           fold_variant: str = "B"):
     """Decode attention of every draft query against its sequence's cache.
 
     Arguments follow the layouts in the module docstring. ``pairs`` optionally
@@ -188,10 +196,12 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int 
                 lse_L = _logsumexp(logits)
                 lse_F = _logsumexp(phi)
                 lse_Fa = _logsumexp(alpha * phi)
-                tot = np.logaddexp(lse_L, beta + lse_F)
+                # log of the far memory's total weight, per parameterisation
+                far_mass = {"B": beta + lse_F, "A": beta + lse_Fa, "B'": beta + lse_Fa / alpha}[fold_variant]
+                tot = np.logaddexp(lse_L, far_mass)
                 with np.errstate(invalid="ignore"):  # -inf - -inf only when a partition is empty
                     w_loc = np.exp(logits - tot[:, None])
-                    w_far = np.exp(beta + lse_F - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])
+                    w_far = np.exp(far_mass - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])
                 o = w_loc @ V + w_far @ Vf
             else:
                 tot = _logsumexp(logits)

@@ -158,7 +158,7 @@ def test_struct_size_reserved_and_theta_checked():
     p.struct_size = 64
     assert call(p) == -1
     p = params()
-    p.reserved = 1
+    p.fold_variant = 3
     assert call(p) == -1
     p = params(mode="fold", n_sink=0, rope_theta=0.0)
     assert call(p, fold=True) == -1

@@ -304,3 +304,20 @@ def test_graph_replay_matches_eager():
         eager = (g["q"].float() * 2).sum()  # unrelated eager work between replays
         torch.cuda.synchronize()
         assert torch.isfinite(eager)
+
+
+@pytest.mark.parametrize("variant", ["A", "B'"])
+def test_fold_parameterisations(variant):
+    # The joint-softmax and virtual-key readings of FOLD's alpha/beta (fold_variant).
+    x = synth.make_inputs(ctx_lens=[20000, 700, 4097, 5], T=6, Hq=16, Hkv=4, d=128, seed=25, fold=True,
+                          needle_frac=0.01)
+    g = to_dev(x)
+    n = np_inputs(x)
+    for alpha, beta, rope in ((1.0, 0.0, "neox"), (2.0, -1.0, "neox"), (4.0, 0.5, "none"), (0.5, 1.0, "neox")):
+        kw = dict(mode="fold", window=4096, alpha=alpha, beta=beta, rope=rope)
+        out, lse = _da().decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=g["k_side"],
+                                ctx_lens=g["ctx_lens"], rope_theta=5e5, fold_variant=variant, **kw)
+        torch.cuda.synchronize()
+        ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"], k_side=n["k_side"],
+                            rope_theta=5e5, fold_variant=variant, **kw)
+        compare(out.cpu().numpy(), lse.cpu().numpy(), ref, f"fold variant {variant} {kw}")

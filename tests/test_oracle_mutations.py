@@ -21,10 +21,11 @@ MUTATIONS = [
     ("rope frequency exponent", "omega = float(theta) ** (-2.0 * np.arange(h", "omega = float(theta) ** (-1.0 * np.arange(h"),
     ("rope pair sign", "x1 * sin + x2 * cos], axis=-1)", "x1 * sin - x2 * cos], axis=-1)"),
     ("rope pairs adjacent channels", "x1, x2 = x[..., :h], x[..., h:]", "x1, x2 = x[..., 0::2], x[..., 1::2]"),
-    ("beta dropped", "tot = np.logaddexp(lse_L, beta + lse_F)\n                with", "tot = np.logaddexp(lse_L, lse_F)\n                with"),
-    ("alpha leaks into the far mass", "w_far = np.exp(beta + lse_F - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])\n                o = w_loc",
-     "w_far = np.exp(beta + lse_Fa - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])\n                o = w_loc"),
+    ("beta dropped", 'far_mass = {"B": beta + lse_F,', 'far_mass = {"B": lse_F,'),
+    ("alpha leaks into the far mass", 'far_mass = {"B": beta + lse_F,', 'far_mass = {"B": beta + lse_Fa,'),
     ("far weights not normalised by Z_Fa", "np.exp(alpha * phi - lse_Fa[:, None])\n                o = w_loc", "np.exp(alpha * phi - lse_F[:, None])\n                o = w_loc"),
+    ("variant A with the unsharpened mass", '"A": beta + lse_Fa,', '"A": beta + lse_F,'),
+    ("variant B' without the 1/alpha", '"B\'": beta + lse_Fa / alpha}', '"B\'": beta + lse_Fa}'),
     ("visible count ignores the window", "n = int(main.size + far.size)\n        c = scale", "n = L\n        c = scale"),
     ("query scale without log", "return 1.0 + float(kappa) * math.log(max(int(n), int(n0)) / int(n0))",
      "return 1.0 + float(kappa) * (max(int(n), int(n0)) / int(n0) - 1)"),

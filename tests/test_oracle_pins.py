@@ -632,3 +632,44 @@ def test_draft_tokens_keep_the_cached_visible_count_for_kappa():
     a = ref.decode_with_draft(q, k, v, table, ctx, "full", kd, vd, kappa=0.4, n0=4)
     b_ = ref.decode_with_draft(q * s, k, v, table, ctx, "full", kd, vd)
     assert np.allclose(a["out"], b_["out"], atol=1e-13) and np.allclose(a["lse"], b_["lse"], atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- FOLD parameterisations
+@pytest.mark.parametrize("variant", ["A", "B'"])
+def test_fold_variants_match_brute_force(variant):
+    ctx = [37, 8, 64, 21]
+    Hkv, G, T, d = 2, 2, 2, 8
+    k, v, ks, table = paged(ctx, Hkv, d, seed=17, side=True)
+    q = np.random.default_rng(23).standard_normal((len(ctx), T, Hkv * G, d)) * 1.5
+    for alpha, beta, W in ((1.0, 0.0, 9), (3.0, -1.0, 9), (0.5, 0.7, 5), (2.0, 0.0, 0)):
+        kw = dict(window=W, alpha=alpha, beta=beta, k_side=ks, rope_theta=100.0, fold_variant=variant)
+        r = ref.decode(q, k, v, table, ctx, "fold", **kw)
+        bo, bl, _ = brute.decode(q, k, v, table, ctx, "fold", **kw)
+        assert np.allclose(r["out"], np.array(bo), atol=1e-12)
+        assert np.allclose(r["lse"], np.array(bl), atol=1e-12)
+
+
+def test_fold_variants_reduce_to_the_union_softmax_and_hand_values():
+    ctx = [60, 30]
+    d = 8
+    k, v, ks, table = paged(ctx, 1, d, seed=18, side=True)
+    q = np.random.default_rng(24).standard_normal((2, 2, 2, d))
+    base = ref.decode(q, k, v, table, ctx, "fold", window=10, alpha=1.0, beta=0.0, k_side=ks)
+    for variant in ("A", "B'"):
+        r = ref.decode(q, k, v, table, ctx, "fold", window=10, alpha=1.0, beta=0.0, k_side=ks, fold_variant=variant)
+        assert np.allclose(r["out"], base["out"], atol=1e-13) and np.allclose(r["lse"], base["lse"], atol=1e-13)
+    # Hand example of test_fold_hand_example (local logit 0, far logits 1 and 0, alpha 2, beta -1):
+    #   A:  lse = ln(1 + e^-1 (e^2 + 1)),  B': lse = ln(1 + e^-1 (e^2 + 1)^(1/2))
+    e = math.e
+    kk = key_pool(1, 1, 8)
+    kside = key_pool(1, 1, 8)
+    put_key(kside, 0, 0, 0, np.eye(8)[0])
+    vv = np.zeros((1, 1, 8, BLOCK)); vv[0, 0, 0, 0] = 1; vv[0, 0, 1, 1] = 1; vv[0, 0, :2, 2] = 3
+    qq = np.eye(8)[0].reshape(1, 1, 1, 8)
+    for variant, mass in (("A", (e * e + 1) / e), ("B'", math.sqrt(e * e + 1) / e)):
+        r = ref.decode(qq, kk, vv, np.array([[0]]), [3], "fold", window=1, alpha=2.0, beta=-1.0, softmax_scale=1.0,
+                       rope="none", k_side=kside, fold_variant=variant)
+        assert abs(r["lse"][0, 0, 0] - math.log(1 + mass)) < 1e-14
+        far_out = np.array([e * e, 1.0] + [0] * 6) / (e * e + 1)
+        want = (np.array([3.0, 3.0] + [0] * 6) + mass * far_out) / (1 + mass)
+        assert np.allclose(r["out"][0, 0, 0], want, atol=1e-14)
