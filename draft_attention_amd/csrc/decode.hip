@@ -567,16 +567,19 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
 
 // ---------------------------------------------------------------- pass 2
 // One workgroup of 256 threads per output row (sequence, kv head, query row).
-// Phase 1 reduces the row's item records to partition maxima and sums; phase 2
-// gathers the unnormalised partial outputs, thread (group g, channel quad c)
-// summing items g, g + NG, ... with per-item scales staged in LDS, so every
-// load of a phase is independent and many are in flight at once. FOLD's
-// partitions are then combined with beta.
+// It reduces the row's item records to partition maxima and sums, scales and
+// sums the unnormalised partial outputs, then combines FOLD's partitions.
+// Rows with at most NG * kFastItems items (every workload here) take one round
+// of loads: each thread issues its statistics record and its partial outputs
+// (thread (group g, channel quad c) owns items g, g + NG, ...) before using any
+// of them. Longer rows stream the records in tiles.
+constexpr int kFastItems = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   constexpr int NQ = D / 4;     // float4 channel quads per row
   constexpr int NG = 256 / NQ;  // item groups
-  constexpr int TILE = 1024;    // items whose scales are staged at once
+  constexpr int TILE = 1024;    // items whose scales are staged at once (long rows)
   __shared__ float s_scale[TILE];
   __shared__ float4 s_part[2][NG][NQ];
   __shared__ float s_red[4][4];
@@ -598,83 +601,133 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   i1 = i1 < lim ? i1 : lim;
   const float alpha = a.alpha;
   const size_t rp = (size_t)a.rows_pad;
+  const int64_t n = i1 - i0;
+  const float* accrow = a.acc + row * (size_t)D + 4 * q4;
 
-  // Phase 1a: maxima of the two partitions.
-  float mM = -INFINITY, mF = -INFINITY;
-  for (int64_t i = i0 + tid; i < i1; i += 256) {
-    const float m = a.stat[(size_t)i * rp + row].x;
-    if (i < im) mM = fmaxf(mM, m);
-    else mF = fmaxf(mF, m);
-  }
+  // block-wide max / sum of per-thread values through the 4 waves
+  auto block_max2 = [&](float& x, float& y) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mM = fmaxf(mM, __shfl_xor(mM, off, 64));
-    mF = fmaxf(mF, __shfl_xor(mF, off, 64));
-  }
-  if (lane == 0) { s_red[wv][0] = mM; s_red[wv][1] = mF; }
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
-  const float MF = fmaxf(fmaxf(s_red[0][1], s_red[1][1]), fmaxf(s_red[2][1], s_red[3][1]));
-  __syncthreads();
-
-  // Phase 1b: partition sums rescaled to the maxima.
-  float Ls = 0.f, ZF = 0.f, ZFa = 0.f;
-  for (int64_t i = i0 + tid; i < i1; i += 256) {
-    const float4 st = a.stat[(size_t)i * rp + row];
-    if (st.x == -INFINITY) continue;
-    if (i < im) {
-      Ls += st.y * exp2f(st.x - M);
-    } else {
-      ZF += st.z * exp2f(st.x - MF);
-      ZFa += st.y * exp2f(alpha * (st.x - MF));
+    for (int off = 32; off >= 1; off >>= 1) {
+      x = fmaxf(x, __shfl_xor(x, off, 64));
+      y = fmaxf(y, __shfl_xor(y, off, 64));
     }
-  }
+    if (lane == 0) { s_red[wv][0] = x; s_red[wv][1] = y; }
+    __syncthreads();
+    x = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
+    y = fmaxf(fmaxf(s_red[0][1], s_red[1][1]), fmaxf(s_red[2][1], s_red[3][1]));
+    __syncthreads();
+  };
+  auto block_sum3 = [&](float& x, float& y, float& z) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Ls += __shfl_xor(Ls, off, 64);
-    ZF += __shfl_xor(ZF, off, 64);
-    ZFa += __shfl_xor(ZFa, off, 64);
-  }
-  if (lane == 0) { s_red[wv][0] = Ls; s_red[wv][1] = ZF; s_red[wv][2] = ZFa; }
-  __syncthreads();
-  Ls = s_red[0][0] + s_red[1][0] + s_red[2][0] + s_red[3][0];
-  ZF = s_red[0][1] + s_red[1][1] + s_red[2][1] + s_red[3][1];
-  ZFa = s_red[0][2] + s_red[1][2] + s_red[2][2] + s_red[3][2];
+    for (int off = 32; off >= 1; off >>= 1) {
+      x += __shfl_xor(x, off, 64);
+      y += __shfl_xor(y, off, 64);
+      z += __shfl_xor(z, off, 64);
+    }
+    if (lane == 0) { s_red[wv][0] = x; s_red[wv][1] = y; s_red[wv][2] = z; }
+    __syncthreads();
+    x = s_red[0][0] + s_red[1][0] + s_red[2][0] + s_red[3][0];
+    y = s_red[0][1] + s_red[1][1] + s_red[2][1] + s_red[3][1];
+    z = s_red[0][2] + s_red[1][2] + s_red[2][2] + s_red[3][2];
+    __syncthreads();
+  };
 
-  // Phase 2: scaled sums of the partial outputs, main items then far items.
-  float4 accp[2];
+  float M, MF, Ls, ZF, ZFa;
+  float4 accp[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (n <= (int64_t)NG * kFastItems) {
+    // one round of loads
+    const bool has_st = tid < n;
+    float4 st = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    if (has_st) st = a.stat[(size_t)(i0 + tid) * rp + row];
+    float4 v[kFastItems];
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int64_t lo = pt == 0 ? i0 : im, hi = pt == 0 ? im : i1;
-    const float ref = pt == 0 ? M : MF;
-    const float sh = pt == 0 ? 1.f : alpha;
-    for (int64_t t0 = lo; t0 < hi; t0 += TILE) {
-      const int64_t t1 = hi < t0 + TILE ? hi : t0 + TILE;
-      __syncthreads();
-      for (int64_t i = t0 + tid; i < t1; i += 256) {
-        const float m = a.stat[(size_t)i * rp + row].x;
-        s_scale[i - t0] = m == -INFINITY ? 0.f : exp2f(sh * (m - ref));
+    for (int k = 0; k < kFastItems; ++k) {
+      const int64_t i = grp + (int64_t)k * NG;
+      v[k] = i < n ? *(const float4*)(accrow + (size_t)(i0 + i) * rp * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const bool is_main = i0 + tid < im;
+    M = has_st && is_main ? st.x : -INFINITY;
+    MF = has_st && !is_main ? st.x : -INFINITY;
+    block_max2(M, MF);
+    float sc = 0.f;
+    Ls = 0.f; ZF = 0.f; ZFa = 0.f;
+    if (has_st && st.x != -INFINITY) {
+      if (is_main) {
+        sc = exp2f(st.x - M);
+        Ls = st.y * sc;
+      } else {
+        sc = exp2f(alpha * (st.x - MF));
+        ZF = st.z * exp2f(st.x - MF);
+        ZFa = st.y * sc;
       }
-      __syncthreads();
-      const float* base = a.acc + row * (size_t)D + 4 * q4;
+    }
+    if (tid < n) s_scale[tid] = sc;
+    block_sum3(Ls, ZF, ZFa);   // its barriers also publish s_scale
+#pragma unroll
+    for (int k = 0; k < kFastItems; ++k) {
+      const int64_t i = grp + (int64_t)k * NG;
+      if (i < n) {
+        const float sk = s_scale[i];
+        float4& acc = (i0 + i < im) ? accp[0] : accp[1];
+        acc.x += sk * v[k].x;
+        acc.y += sk * v[k].y;
+        acc.z += sk * v[k].z;
+        acc.w += sk * v[k].w;
+      }
+    }
+  } else {
+    // long rows: maxima, sums, then the partial outputs tile by tile
+    M = -INFINITY;
+    MF = -INFINITY;
+    for (int64_t i = i0 + tid; i < i1; i += 256) {
+      const float m = a.stat[(size_t)i * rp + row].x;
+      if (i < im) M = fmaxf(M, m);
+      else MF = fmaxf(MF, m);
+    }
+    block_max2(M, MF);
+    Ls = 0.f; ZF = 0.f; ZFa = 0.f;
+    for (int64_t i = i0 + tid; i < i1; i += 256) {
+      const float4 st = a.stat[(size_t)i * rp + row];
+      if (st.x == -INFINITY) continue;
+      if (i < im) {
+        Ls += st.y * exp2f(st.x - M);
+      } else {
+        ZF += st.z * exp2f(st.x - MF);
+        ZFa += st.y * exp2f(alpha * (st.x - MF));
+      }
+    }
+    block_sum3(Ls, ZF, ZFa);
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t lo = pt == 0 ? i0 : im, hi = pt == 0 ? im : i1;
+      const float ref = pt == 0 ? M : MF;
+      const float sh = pt == 0 ? 1.f : alpha;
+      for (int64_t t0 = lo; t0 < hi; t0 += TILE) {
+        const int64_t t1 = hi < t0 + TILE ? hi : t0 + TILE;
+        __syncthreads();
+        for (int64_t i = t0 + tid; i < t1; i += 256) {
+          const float m = a.stat[(size_t)i * rp + row].x;
+          s_scale[i - t0] = m == -INFINITY ? 0.f : exp2f(sh * (m - ref));
+        }
+        __syncthreads();
 #pragma unroll 8
-      for (int64_t i = t0 + grp; i < t1; i += NG) {
-        const float4 v = *(const float4*)(base + (size_t)i * rp * D);
-        const float sc = s_scale[i - t0];
-        acc.x += sc * v.x;
-        acc.y += sc * v.y;
-        acc.z += sc * v.z;
-        acc.w += sc * v.w;
+        for (int64_t i = t0 + grp; i < t1; i += NG) {
+          const float4 v = *(const float4*)(accrow + (size_t)i * rp * D);
+          const float sc = s_scale[i - t0];
+          acc.x += sc * v.x;
+          acc.y += sc * v.y;
+          acc.z += sc * v.z;
+          acc.w += sc * v.w;
+        }
       }
+      accp[pt] = acc;
     }
-    accp[pt] = acc;
   }
   s_part[0][grp][q4] = accp[0];
   s_part[1][grp][q4] = accp[1];
   __syncthreads();
 
-  // Final combine: thread c < D owns output channel c.
   // log2 weights of the partitions. The far memory weighs e^beta Z_F (default),
   // e^beta Z_Fa (joint softmax) or e^beta Z_Fa^(1/alpha) (one virtual key); in
   // the log2 domain Z_F = 2^MF ZF and Z_Fa = 2^(alpha MF) ZFa.
@@ -690,6 +743,7 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   const int32_t t = row / a.G;
   const int32_t head = kvh * a.G + (row - t * a.G);
   const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
+  // Final combine: thread c < D owns output channel c.
   if (tid < D) {
     const float* pm = (const float*)&s_part[0][0][0];
     const float* pf = (const float*)&s_part[1][0][0];
