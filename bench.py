@@ -2,11 +2,13 @@
 """Bench: draft-head decode attention over a very long paged KV cache, one MI355X.
 
 One step = one draft_attn_decode call: the device-side work decomposition, the
-split-K streaming pass over every visible K/V block and the log-sum-exp merge.
-Inputs (seeded, synthetic, bf16) are resident in HBM before timing starts. Each
-timed step is one eager call through a prepared binding (arguments marshalled
-once, one C call per step). --graph instead times replays of the call captured
-in a HIP graph; on this software stack a replay costs more than an eager call.
+split-K streaming pass over every visible K/V block and the log-sum-exp merge
+(a second kernel, or the tail of the streaming kernel on the single-launch
+path, which the library picks for small steps). Inputs (seeded, synthetic,
+bf16) are resident in HBM before timing starts. Each timed step is one eager
+call through a prepared binding (arguments marshalled once, one C call per
+step). --graph instead times replays of the call captured in a HIP graph; on
+this software stack a replay costs more than an eager call.
 
 Default workload: the million-token draft step (1 sequence, 2^20 cached keys in
 16-token blocks behind a shuffled block table, 32 query / 8 kv heads, d = 128,
@@ -14,7 +16,8 @@ Default workload: the million-token draft step (1 sequence, 2^20 cached keys in
 cache -- the read that grows with context. Printed: one JSON line with
   value       KV GB/s of the whole step (algorithmic K+V bytes / wall time)
   roofline    the streaming pass alone: algorithmic bytes / its mean duration
-              (HIP events recorded by the library around that launch), against
+              (HIP events recorded by the library around that launch, in a
+              second loop of the same calls so the timed steps carry none), against
               the 8 TB/s HBM peak; traffic = FETCH_SIZE + WRITE_SIZE bytes per
               launch from rocprofv3 counters (profiles/traffic.json), when they
               were taken on the current kernel source
@@ -49,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default="needles_1m")
     ap.add_argument("--run", type=int, default=0, help="index into the workload's mode list")
     ap.add_argument("--split-keys", type=int, default=0)
+    ap.add_argument("--launch", default="auto", choices=["auto", "two_pass", "single"])
+    ap.add_argument("--window", type=int, default=None, help="override the run's window (window / fold modes)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -111,7 +116,7 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes": n, "launches": 3}), flush=True)
 
 
-def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False):
+def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False, launch="auto"):
     """Generate inputs on the GPU, time `steps` decode calls; returns a result dict."""
     import torch
 
@@ -127,15 +132,16 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
     p = da.make_params(num_seqs=len(w.ctx_lens), num_draft_tokens=w.T, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
                        head_dim=w.d, num_blocks=x["k_cache"].shape[0],
                        max_blocks_per_seq=x["block_table"].shape[1], split_keys=split, rope_theta=w.rope_theta,
-                       **kw)
+                       launch=launch, **kw)
     ws = torch.empty(da.workspace_size(p, w.ctx_lens), dtype=torch.uint8, device=dev)
     _, chunk = da.plan(p, w.ctx_lens)
+    launch_used = da.launch_of(p, w.ctx_lens)
     ev = HipEvents() if want_events else None
     pairs = [(ev.create(), ev.create()) for _ in range(steps)] if ev else [None] * steps
 
     call = da.prepare(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], k_side=side,
                       ctx_lens=w.ctx_lens, out=out, lse=lse, workspace=ws, rope_theta=w.rope_theta,
-                      split_keys=split, **kw)
+                      split_keys=split, launch=launch, **kw)
 
     def step(pe):
         call(prof_events=pe)
@@ -143,15 +149,19 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
-    # Eager steps, with the streaming pass bracketed by HIP events.
+    # Timed eager steps.
     t0 = time.perf_counter()
     for k in range(steps):
-        step(pairs[k])
+        step(None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_eager = (t1 - t0) * 1e3 / steps
     pass1 = None
     if ev:
+        # The same calls again, the streaming kernel bracketed by HIP events.
+        for k in range(steps):
+            step(pairs[k])
+        torch.cuda.synchronize()
         durs = [ev.elapsed_ms(a, b) for a, b in pairs]
         pass1 = sum(durs) / len(durs)
         for a, b in pairs:
@@ -183,7 +193,7 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
     keys = sum(visible_keys(L, **kw) for L in w.ctx_lens) * w.Hkv
     bytes_ = keys * 4 * w.d
     res = dict(x=x, kw=kw, ms=ms, ms_eager=ms_eager, pass1_ms=pass1, bytes=bytes_, keys=keys // w.Hkv, chunk=chunk,
-               torch_ok=bool(torch.isfinite(out).all().item()))
+               launch=launch_used, torch_ok=bool(torch.isfinite(out).all().item()))
     return res
 
 
@@ -244,8 +254,11 @@ def main():
 
     wl = synth.workloads(args.seed)
     w = wl[args.workload]
-    kw = w.runs[args.run]
-    r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys, graph=args.graph)
+    kw = dict(w.runs[args.run])
+    if args.window is not None:
+        kw["window"] = args.window
+    r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys, graph=args.graph,
+                      launch=args.launch)
     gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
     p1 = r["bytes"] / (r["pass1_ms"] * 1e-3) / 1e9
     tag = f"{w.name}/{kw['mode']}"
@@ -281,7 +294,8 @@ def main():
         "config": {"workload": w.name, "mode": mode_str, "num_seqs": len(w.ctx_lens),
                    "ctx_len": w.ctx_lens[0] if len(w.ctx_lens) == 1 else w.ctx_lens,
                    "draft_tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "block_size": 16,
-                   "split_keys": r["chunk"], "alpha": kw.get("alpha", 1.0), "beta": kw.get("beta", 0.0),
+                   "split_keys": r["chunk"], "launch": r["launch"],
+                   "alpha": kw.get("alpha", 1.0), "beta": kw.get("beta", 0.0),
                    "kappa": kw.get("kappa", 0.0)},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "draft_steps_per_s": round(1e3 / r["ms"], 2),
@@ -289,7 +303,9 @@ def main():
         "kv_bytes_per_step": r["bytes"],
         "roofline": {"bound": "hbm", "achieved": round(p1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(p1 / HBM_PEAK_GBS, 4), "traffic": traffic_for(tag),
-                     "kernel": "pass1_kernel (split-K K/V streaming)", "mean_launch_ms": round(r["pass1_ms"], 5)},
+                     "kernel": ("pass1_kernel (split-K K/V streaming)" if r["launch"] == "two_pass" else
+                                "pass1_kernel (split-K K/V streaming + in-kernel merge, single launch)"),
+                     "mean_launch_ms": round(r["pass1_ms"], 5)},
         "secondary": secondary,
         "cpu_baseline": cpu,
     }

@@ -19,11 +19,16 @@ FULL, WINDOW, FOLD = 0, 1, 2
 ROPE_NEOX, ROPE_NONE = 0, 1
 OK, EINVAL, ENOSPC, EHIP, ENOTSUP = 0, -1, -2, -3, -4
 MAX_ROWS = 32
-ABI_VERSION = 1
+ABI_VERSION = 2
 _MODES = {"full": FULL, "window": WINDOW, "fold": FOLD}
 _ROPES = {"neox": ROPE_NEOX, "none": ROPE_NONE}
 FOLD_B, FOLD_JOINT, FOLD_VIRTUAL = 0, 1, 2
 _FOLD_VARIANTS = {"B": FOLD_B, "A": FOLD_JOINT, "B'": FOLD_VIRTUAL}
+LAUNCH_AUTO, LAUNCH_TWO_PASS, LAUNCH_SINGLE = 0, 1, 2
+_LAUNCHES = {"auto": LAUNCH_AUTO, "two_pass": LAUNCH_TWO_PASS, "single": LAUNCH_SINGLE}
+OUT_F32, OUT_BF16 = 0, 1
+_OUT_DTYPES = {"f32": OUT_F32, "bf16": OUT_BF16}
+MAX_GROUP_ITEMS = 64
 
 
 class Params(ctypes.Structure):
@@ -53,6 +58,8 @@ class Params(ctypes.Structure):
         ("prof_events", ctypes.c_void_p * 2),
         ("split_keys", ctypes.c_int32),
         ("fold_variant", ctypes.c_int32),
+        ("launch", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
     ]
 
 
@@ -98,7 +105,7 @@ def _load():
     lib.draft_attn_workspace_size.restype = ctypes.c_int
     lib.draft_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, ctypes.c_size_t, vp]
     lib.draft_attn_decode.restype = ctypes.c_int
-    lib.draft_attn_plan.argtypes = [P, i32p, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), i32p]
+    lib.draft_attn_plan.argtypes = [P, i32p, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), i32p, i32p]
     lib.draft_attn_plan.restype = ctypes.c_int
     lib.draft_attn_merge_draft.argtypes = [P, vp, vp, vp, vp, i32p, vp, vp, vp]
     lib.draft_attn_merge_draft.restype = ctypes.c_int
@@ -118,7 +125,7 @@ def _load():
     lib.draft_attn_version.restype = ctypes.c_int
     if lib.draft_attn_version() != ABI_VERSION:
         raise ImportError("libdraft_attn.so ABI version mismatch")
-    if ctypes.sizeof(Params) != 120 or ctypes.sizeof(AppendParams) != 48:
+    if ctypes.sizeof(Params) != 128 or ctypes.sizeof(AppendParams) != 48:
         raise ImportError("params mirror has the wrong size")
     return lib
 
@@ -133,7 +140,8 @@ def strerror(status: int) -> str:
 def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks,
                 max_blocks_per_seq, mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0,
                 n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, split_keys=0,
-                debug_visit=0, debug_visit_stride=0, prof_events=None, fold_variant="B") -> Params:
+                debug_visit=0, debug_visit_stride=0, prof_events=None, fold_variant="B", launch="auto",
+                out_dtype="f32") -> Params:
     p = Params()
     lib.draft_attn_params_init(ctypes.byref(p))
     p.num_seqs = int(num_seqs)
@@ -157,12 +165,29 @@ def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_d
     p.rope_theta = float(rope_theta)
     p.split_keys = int(split_keys)
     p.fold_variant = _FOLD_VARIANTS[fold_variant] if isinstance(fold_variant, str) else int(fold_variant)
+    p.launch = _LAUNCHES[launch] if isinstance(launch, str) else int(launch)
+    p.out_dtype = _out_code(out_dtype)
     p.debug_visit = int(debug_visit) or None
     p.debug_visit_stride = int(debug_visit_stride)
     if prof_events is not None:
         p.prof_events[0] = int(prof_events[0])
         p.prof_events[1] = int(prof_events[1])
     return p
+
+
+def _out_code(out_dtype) -> int:
+    """out_dtype given as "f32" / "bf16", a torch dtype, or the header's code."""
+    if isinstance(out_dtype, str):
+        return _OUT_DTYPES[out_dtype]
+    if isinstance(out_dtype, int):
+        return out_dtype
+    import torch
+    return {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+
+
+def _out_torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == OUT_BF16 else torch.float32
 
 
 def _host_i32(values):
@@ -183,16 +208,26 @@ def plan(params: Params, ctx_lens):
     host = _host_i32(ctx_lens)
     total = ctypes.c_int64(0)
     chunk = ctypes.c_int32(0)
-    st = lib.draft_attn_plan(ctypes.byref(params), host, None, 0, ctypes.byref(total), ctypes.byref(chunk))
+    st = lib.draft_attn_plan(ctypes.byref(params), host, None, 0, ctypes.byref(total), ctypes.byref(chunk), None)
     if st != OK:
         raise DraftAttnError(st, "draft_attn_plan")
     buf = (ctypes.c_int32 * (5 * max(total.value, 1)))()
     st = lib.draft_attn_plan(ctypes.byref(params), host, buf, total.value, ctypes.byref(total),
-                             ctypes.byref(chunk))
+                             ctypes.byref(chunk), None)
     if st != OK:
         raise DraftAttnError(st, "draft_attn_plan")
     items = [tuple(buf[5 * i:5 * i + 5]) for i in range(total.value)]
     return items, int(chunk.value)
+
+
+def launch_of(params: Params, ctx_lens) -> str:
+    """Launch shape a call with these params and lengths uses: "two_pass" or "single"."""
+    total, chunk, launch = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib.draft_attn_plan(ctypes.byref(params), _host_i32(ctx_lens), None, 0, ctypes.byref(total),
+                             ctypes.byref(chunk), ctypes.byref(launch))
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_plan")
+    return "single" if launch.value == LAUNCH_SINGLE else "two_pass"
 
 
 class PreparedDecode:
@@ -218,7 +253,7 @@ class PreparedDecode:
 def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
             beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
             ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
-            debug_visit=None, fold_variant="B") -> PreparedDecode:
+            debug_visit=None, fold_variant="B", launch="auto", out_dtype="f32") -> PreparedDecode:
     """Marshal the arguments of decode() once (same meaning as there)."""
     import torch
 
@@ -234,10 +269,10 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
                     window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
                     softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                     split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
-                    fold_variant=fold_variant)
+                    fold_variant=fold_variant, launch=launch, out_dtype=out_dtype)
     dev = q.device
     if out is None:
-        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+        out = torch.empty((B, T, Hq, d), dtype=_out_torch_dtype(p.out_dtype), device=dev)
     if lse is None:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
     need = workspace_size(p, ctx_lens)
@@ -255,13 +290,14 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
 def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
            beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
            ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
-           debug_visit=None, prof_events=None, fold_variant="B"):
+           debug_visit=None, prof_events=None, fold_variant="B", launch="auto", out_dtype="f32"):
     """Enqueue draft_attn_decode on the current (or given) stream; returns (out, lse).
 
     q bf16 [B,T,Hq,d]; k_cache / k_side bf16 [NB,Hkv,d/8,16,8]; v_cache bf16 [NB,Hkv,d,16];
     block_table int32 [B,MB]; ctx_len int32 [B] on the device; ctx_lens: the same
     lengths as a host list (read from ctx_len when omitted, which synchronises).
-    out / lse / workspace are allocated with torch when not given.
+    out / lse / workspace are allocated with torch when not given. launch: "auto",
+    "two_pass" or "single"; out_dtype: "f32" or "bf16" (the dtype of out).
     """
     import torch
 
@@ -277,10 +313,11 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
                     window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
                     softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                     split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
-                    prof_events=prof_events, fold_variant=fold_variant)
+                    prof_events=prof_events, fold_variant=fold_variant, launch=launch,
+                    out_dtype=out_dtype)
     dev = q.device
     if out is None:
-        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+        out = torch.empty((B, T, Hq, d), dtype=_out_torch_dtype(p.out_dtype), device=dev)
     if lse is None:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
     need = workspace_size(p, ctx_lens)

@@ -32,6 +32,7 @@
 // Pass 2 merges the per-item (max, sums, unnormalised output) records with the
 // log-sum-exp rule, then combines FOLD's local and far partitions with beta.
 #include <hip/hip_runtime.h>
+
 #include <math.h>
 #include <stdint.h>
 
@@ -58,9 +59,13 @@ struct Pass1Args {
   float* acc;        // [items][rows_pad][D]: unnormalised partial outputs
   uint8_t* visit;    // optional [B][visit_stride]
   int64_t visit_stride;
+  unsigned long long* flags;  // [items] done flags (single launch)
+  void* out;         // [B][T][Hq][D] fp32 or bf16 (single launch)
+  float* lse;        // [B][T][Hq] (single launch)
   int32_t B, T, Hq, Hkv, G, R, rows_pad, max_blocks, num_blocks;
   int32_t mode, W, S, n0, C, rope, total_items;
-  float alpha, kappa, scale;
+  int32_t out_bf16, fold_variant;
+  float alpha, kappa, scale, beta;
   double omega[kMaxHalfDim];  // RoPE frequencies rope_theta^(-2i/d)
 };
 
@@ -68,10 +73,10 @@ struct Pass2Args {
   const float4* stat;
   const float* acc;
   const int32_t* ctx_len;
-  float* out;
+  void* out;
   float* lse;
   int32_t B, T, Hq, Hkv, G, R, rows_pad;
-  int32_t mode, W, S, C, total_items, fold_variant;
+  int32_t mode, W, S, C, total_items, fold_variant, out_bf16;
   float alpha, beta;
 };
 
@@ -400,7 +405,204 @@ __host__ __device__ inline size_t pass1_lds_bytes(int32_t C, int32_t rows_pad, i
          (size_t)2 * rows_pad * (D + 4) * sizeof(float);
 }
 
-template <int D, int RT, bool FOLDK>
+// Record access on the single-launch path. Work items of one group run on
+// different XCDs, whose L2 caches are not coherent with each other. Records
+// are therefore written and read as 8-byte device-scope accesses, which go to
+// the device's coherence point directly, instead of plain accesses behind
+// device-scope fences, which write back or invalidate a whole L2 each time.
+// Each pair of floats travels as one 64-bit word.
+__device__ __forceinline__ void store_dev4(float* p, float x, float y, float z, float w) {
+  unsigned long long* q = (unsigned long long*)p;
+  __hip_atomic_store(q, ((unsigned long long)__float_as_uint(y) << 32) | __float_as_uint(x), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, ((unsigned long long)__float_as_uint(w) << 32) | __float_as_uint(z), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float4 load_dev4(const float* p) {
+  unsigned long long* q = (unsigned long long*)p;
+  const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
+                     __uint_as_float((uint32_t)(b >> 32)));
+}
+
+// Partition weights of one query row from its reduced statistics (log2 domain:
+// main maximum M and sum Ls; far maximum MF, plain sum ZF and sharpened sum
+// ZFa). The local window weighs Z_L = 2^M Ls; the far memory weighs e^beta Z_F
+// (default), e^beta Z_Fa (joint softmax) or e^beta Z_Fa^(1/alpha) (one virtual
+// key), with Z_F = 2^MF ZF and Z_Fa = 2^(alpha MF) ZFa. Returns the factors fl
+// and ff that turn the scaled partial-output sums of each partition into the
+// output, and the row's lse (natural log).
+struct RowCombine {
+  float fl, ff, lse;
+};
+__device__ __forceinline__ RowCombine combine_row(float M, float MF, float Ls, float ZF, float ZFa, float alpha,
+                                                  float beta, int32_t fold_variant) {
+  const float lwL = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
+  float lwF = -INFINITY;
+  if (ZF > 0.f) {
+    const float far_log2 = fold_variant == DRAFT_ATTN_FOLD_JOINT     ? alpha * MF + log2f(ZFa)
+                           : fold_variant == DRAFT_ATTN_FOLD_VIRTUAL ? MF + log2f(ZFa) / alpha
+                                                                     : MF + log2f(ZF);
+    lwF = beta * kLog2e + far_log2;
+  }
+  const float top = fmaxf(lwL, lwF);
+  RowCombine r{0.f, 0.f, -INFINITY};
+  if (top != -INFINITY) {
+    const float wL = exp2f(lwL - top), wF = exp2f(lwF - top);
+    const float den = wL + wF;
+    r.fl = wL > 0.f ? wL / (den * Ls) : 0.f;
+    r.ff = wF > 0.f ? wF / (den * ZFa) : 0.f;
+    r.lse = (top + log2f(den)) * kLn2;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void store_out4(void* out, bool bf16, int64_t off, float4 v) {
+  if (bf16) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h;
+    h[0] = (__bf16)v.x;
+    h[1] = (__bf16)v.y;
+    h[2] = (__bf16)v.z;
+    h[3] = (__bf16)v.w;
+    *(bf16x4*)((__bf16*)out + off) = h;
+  } else {
+    *(float4*)((float*)out + off) = v;
+  }
+}
+
+// ---------------------------------------------------------------- single-launch merge
+// Run by a workgroup that found every item of its (sequence, kv head) done: it
+// merges the group's n item records (items i0 .. i0 + n - 1, the first nm of
+// them local) into out and lse for every query row of the group. Thread
+// (row = tid / 8, sub = tid % 8) reduces the statistics of items sub, sub + 8,
+// ... of one row and stages each item's final scale in s_sc; then thread tid
+// sums the partial outputs of the (row, channel quad) pairs tid + 256 j, 16
+// float4 loads per thread and round.
+constexpr int kGroupItems = DRAFT_ATTN_MAX_GROUP_ITEMS;
+// Done-flag value: an arbitrary 64-bit pattern (the first 64 fraction bits of
+// sqrt(2)), which plain data left in a workspace is not expected to hold.
+constexpr unsigned long long kDoneFlag = 0x6A09E667F3BCC908ull;
+
+template <int D, int RT>
+__device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int32_t kvh, int64_t i0, int32_t n,
+                                             int32_t nm, float* s_sc) {
+  constexpr int NQ = D / 4;
+  constexpr int ROWS = 16 * RT;
+  constexpr int NPJ = ROWS * NQ / 256;  // (row, channel quad) pairs per thread
+  constexpr int IB = 16 / NPJ;          // items per round of partial-output loads
+  constexpr int SPT = kGroupItems / 8;
+  static_assert(NPJ * 256 == ROWS * NQ, "pairs must tile the workgroup");
+  const int tid = threadIdx.x;
+  const size_t rp = (size_t)a.rows_pad;
+  const int row = tid >> 3, sub = tid & 7;
+  const bool row_ok = row < a.R;
+  const float alpha = a.alpha;
+
+  float4 v[NPJ][IB];
+  auto load_round = [&](int32_t ib) {
+#pragma unroll
+    for (int j = 0; j < NPJ; ++j) {
+      const int pair = tid + 256 * j;
+      const int prow = pair / NQ, q4 = pair - prow * NQ;
+#pragma unroll
+      for (int k = 0; k < IB; ++k) {
+        const int32_t it = ib + k;
+        v[j][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (prow < a.R && it < n) v[j][k] = load_dev4(a.acc + ((size_t)(i0 + it) * rp + prow) * D + 4 * q4);
+      }
+    }
+  };
+  // The first round does not depend on the statistics: issue it first.
+  load_round(0);
+  float4 st[SPT];
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int it = sub + 8 * k;
+    st[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    if (row_ok && it < n) st[k] = load_dev4((const float*)&a.stat[(size_t)(i0 + it) * rp + row]);
+  }
+  float M = -INFINITY, MF = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    if (sub + 8 * k < nm) M = fmaxf(M, st[k].x);
+    else MF = fmaxf(MF, st[k].x);
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    M = fmaxf(M, __shfl_xor(M, off, 64));
+    MF = fmaxf(MF, __shfl_xor(MF, off, 64));
+  }
+  float Ls = 0.f, ZF = 0.f, ZFa = 0.f;
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const float m = st[k].x;
+    if (m == -INFINITY) continue;
+    if (sub + 8 * k < nm) {
+      Ls += st[k].y * exp2f(m - M);
+    } else {
+      ZF += st[k].z * exp2f(m - MF);
+      ZFa += st[k].y * exp2f(alpha * (m - MF));
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    Ls += __shfl_xor(Ls, off, 64);
+    ZF += __shfl_xor(ZF, off, 64);
+    ZFa += __shfl_xor(ZFa, off, 64);
+  }
+  const RowCombine cb = combine_row(M, MF, Ls, ZF, ZFa, alpha, a.beta, a.fold_variant);
+  if (row < ROWS) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int it = sub + 8 * k;
+      if (it >= n) continue;
+      const float m = st[k].x;
+      float sc = 0.f;
+      if (m != -INFINITY) sc = it < nm ? exp2f(m - M) * cb.fl : exp2f(alpha * (m - MF)) * cb.ff;
+      s_sc[row * kGroupItems + it] = sc;
+    }
+  }
+  auto out_row = [&](int32_t r) {
+    const int32_t t = r / a.G;
+    const int32_t head = kvh * a.G + (r - t * a.G);
+    return (int64_t)(b * a.T + t) * a.Hq + head;
+  };
+  if (sub == 0 && row_ok) a.lse[out_row(row)] = cb.lse;
+  __syncthreads();
+
+  float4 acc[NPJ];
+#pragma unroll
+  for (int j = 0; j < NPJ; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int32_t ib = 0; ib < n; ib += IB) {
+    if (ib > 0) load_round(ib);
+#pragma unroll
+    for (int j = 0; j < NPJ; ++j) {
+      const int prow = (tid + 256 * j) / NQ;
+#pragma unroll
+      for (int k = 0; k < IB; ++k) {
+        const int32_t it = ib + k;
+        if (prow < a.R && it < n) {
+          const float sc = s_sc[prow * kGroupItems + it];
+          acc[j].x += sc * v[j][k].x;
+          acc[j].y += sc * v[j][k].y;
+          acc[j].z += sc * v[j][k].z;
+          acc[j].w += sc * v[j][k].w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NPJ; ++j) {
+    const int pair = tid + 256 * j;
+    const int prow = pair / NQ, q4 = pair - prow * NQ;
+    if (prow < a.R) store_out4(a.out, a.out_bf16 != 0, out_row(prow) * D + 4 * q4, acc[j]);
+  }
+}
+
+template <int D, int RT, bool FOLDK, bool SINGLE>
 __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
   constexpr int KS = D / 32, NT = D / 16, OS = D + 4;  // OS: padded LDS row stride (floats)
   extern __shared__ __align__(16) unsigned char smem[];
@@ -551,7 +753,10 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
     const int32_t row = idx / (D / 4), q4 = idx - row * (D / 4);
     const f32x4 v0 = *(const f32x4*)(s_o + row * OS + 4 * q4);
     const f32x4 v1 = *(const f32x4*)(s_o + (rp + row) * OS + 4 * q4);
-    *(f32x4*)(a.acc + (rowbase + row) * D + 4 * q4) = v0 + v1;
+    const f32x4 v = v0 + v1;
+    float* dst = a.acc + (rowbase + row) * D + 4 * q4;
+    if constexpr (SINGLE) store_dev4(dst, v[0], v[1], v[2], v[3]);
+    else *(f32x4*)dst = v;
   }
   if (tid < a.R) {
     float M = s_m[tid], Lsum = 0.f, L1sum = 0.f;
@@ -561,7 +766,40 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
       Lsum += s_l[k * rp + tid].x;
       L1sum += s_l[k * rp + tid].y;
     }
-    a.stat[rowbase + tid] = make_float4(M, Lsum, L1sum, 0.f);
+    if constexpr (SINGLE) store_dev4((float*)&a.stat[rowbase + tid], M, Lsum, L1sum, 0.f);
+    else a.stat[rowbase + tid] = make_float4(M, Lsum, L1sum, 0.f);
+  }
+  if constexpr (SINGLE) {
+    // Mark this item done, then look at the done flags of the whole group; a
+    // workgroup that finds them all set merges the group and clears them. Each
+    // workgroup's flag store completes before it reads the flags, so of any two
+    // late workgroups the second sees the first's flag: at least one merges.
+    // Rarely two see all flags at once; both merge and write the same result.
+    // Flags hold kDoneFlag or 0 (every call leaves them 0); any other value,
+    // as in a fresh workspace, reads as not done.
+    __shared__ int s_last;
+    const int64_t g0 = (int64_t)si.base + (int64_t)kvh * si.n;  // first item of the group
+    const bool mergeable = si.n <= kGroupItems && g0 + si.n <= (int64_t)a.total_items;
+    // Each wave waits until its record stores have completed (s_waitcnt
+    // vmcnt(0); expcnt and lgkmcnt left unconstrained) before the barrier.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (wave == 0) {
+      int last = 0;
+      if (mergeable) {
+        if (lane == 0) __hip_atomic_store(a.flags + w, kDoneFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        unsigned long long f = kDoneFlag;
+        if (lane < si.n) f = __hip_atomic_load(a.flags + g0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = __ballot(f != kDoneFlag) == 0ull;
+        if (last && lane < si.n) __hip_atomic_store(a.flags + g0 + lane, 0ull, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    single_merge<D, RT>(a, b, kvh, g0, si.n, si.n_main, s_o);
   }
 }
 
@@ -728,18 +966,7 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   s_part[1][grp][q4] = accp[1];
   __syncthreads();
 
-  // log2 weights of the partitions. The far memory weighs e^beta Z_F (default),
-  // e^beta Z_Fa (joint softmax) or e^beta Z_Fa^(1/alpha) (one virtual key); in
-  // the log2 domain Z_F = 2^MF ZF and Z_Fa = 2^(alpha MF) ZFa.
-  const float lwL = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
-  float lwF = -INFINITY;
-  if (ZF > 0.f) {
-    const float far_log2 = a.fold_variant == DRAFT_ATTN_FOLD_JOINT     ? alpha * MF + log2f(ZFa)
-                           : a.fold_variant == DRAFT_ATTN_FOLD_VIRTUAL ? MF + log2f(ZFa) / alpha
-                                                                       : MF + log2f(ZF);
-    lwF = a.beta * kLog2e + far_log2;
-  }
-  const float top = fmaxf(lwL, lwF);
+  const RowCombine cb = combine_row(M, MF, Ls, ZF, ZFa, alpha, a.beta, a.fold_variant);
   const int32_t t = row / a.G;
   const int32_t head = kvh * a.G + (row - t * a.G);
   const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
@@ -753,32 +980,23 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
       sm += pm[g2 * D + tid];
       sf += pf[g2 * D + tid];
     }
-    float res = 0.f;
-    if (top != -INFINITY) {
-      const float wL = exp2f(lwL - top), wF = exp2f(lwF - top);
-      const float den = wL + wF;
-      const float fl = wL > 0.f ? wL / (den * Ls) : 0.f;
-      const float ff = wF > 0.f ? wF / (den * ZFa) : 0.f;
-      res = sm * fl + sf * ff;
-    }
-    a.out[orow * D + tid] = res;
+    const float res = sm * cb.fl + sf * cb.ff;
+    if (a.out_bf16) ((__bf16*)a.out)[orow * D + tid] = (__bf16)res;
+    else ((float*)a.out)[orow * D + tid] = res;
   }
-  if (tid == 0) {
-    const float den = exp2f(lwL - top) + exp2f(lwF - top);
-    a.lse[orow] = top == -INFINITY ? -INFINITY : (top + log2f(den)) * kLn2;
-  }
+  if (tid == 0) a.lse[orow] = cb.lse;
 }
 
 // ---------------------------------------------------------------- launch
-template <int D>
+template <int D, bool SINGLE>
 static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t grid, size_t lds,
                          hipStream_t s) {
   if (row_tiles == 1) {
-    if (fold) pass1_kernel<D, 1, true><<<grid, 64 * kWaves, lds, s>>>(a);
-    else pass1_kernel<D, 1, false><<<grid, 64 * kWaves, lds, s>>>(a);
+    if (fold) pass1_kernel<D, 1, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
+    else pass1_kernel<D, 1, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
   } else {
-    if (fold) pass1_kernel<D, 2, true><<<grid, 64 * kWaves, lds, s>>>(a);
-    else pass1_kernel<D, 2, false><<<grid, 64 * kWaves, lds, s>>>(a);
+    if (fold) pass1_kernel<D, 2, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
+    else pass1_kernel<D, 2, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
   }
 }
 
@@ -786,7 +1004,7 @@ static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t 
 
 extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
                                  const void* v_cache, const void* k_side, const int32_t* block_table,
-                                 const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out,
+                                 const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
                                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace da;
   Prepared pr;
@@ -816,6 +1034,12 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a1.acc = (float*)(ws + pr.acc_offset);
   a1.visit = p->debug_visit;
   a1.visit_stride = p->debug_visit_stride;
+  a1.flags = (unsigned long long*)(ws + pr.flag_offset);
+  a1.out = out;
+  a1.lse = lse;
+  a1.out_bf16 = p->out_dtype == DRAFT_ATTN_OUT_BF16;
+  a1.fold_variant = p->fold_variant;
+  a1.beta = p->beta;
   a1.B = p->num_seqs;
   a1.T = p->num_draft_tokens;
   a1.Hq = p->num_q_heads;
@@ -859,20 +1083,32 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a2.alpha = p->alpha;
   a2.beta = p->beta;
   a2.fold_variant = p->fold_variant;
+  a2.out_bf16 = a1.out_bf16;
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();  // clear a stale error so the check below reports ours
   if (p->prof_events[0]) (void)hipEventRecord((hipEvent_t)p->prof_events[0], s);
+  // Every (sequence, kv head) has at least one item, so the single kernel
+  // writes every output row.
+  const bool single = pr.single && pr.total_items > 0;
   if (pr.total_items > 0) {
     const size_t lds = pass1_lds_bytes(pr.chunk, pr.rows_pad, D);
     const bool fold = p->mode == kFold;
-    if (D == 64) launch_pass1<64>(a1, pr.row_tiles, fold, (uint32_t)pr.total_items, lds, s);
-    else launch_pass1<128>(a1, pr.row_tiles, fold, (uint32_t)pr.total_items, lds, s);
+    const uint32_t grid = (uint32_t)pr.total_items;
+    if (single) {
+      if (D == 64) launch_pass1<64, true>(a1, pr.row_tiles, fold, grid, lds, s);
+      else launch_pass1<128, true>(a1, pr.row_tiles, fold, grid, lds, s);
+    } else {
+      if (D == 64) launch_pass1<64, false>(a1, pr.row_tiles, fold, grid, lds, s);
+      else launch_pass1<128, false>(a1, pr.row_tiles, fold, grid, lds, s);
+    }
   }
   if (p->prof_events[1]) (void)hipEventRecord((hipEvent_t)p->prof_events[1], s);
-  const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
-  if (D == 64) pass2_kernel<64><<<rows_total, 256, 0, s>>>(a2);
-  else pass2_kernel<128><<<rows_total, 256, 0, s>>>(a2);
+  if (!single) {
+    const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
+    if (D == 64) pass2_kernel<64><<<rows_total, 256, 0, s>>>(a2);
+    else pass2_kernel<128><<<rows_total, 256, 0, s>>>(a2);
+  }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
 }

@@ -104,6 +104,7 @@ extern "C" int draft_attn_merge_draft(const draft_attn_params* p, const void* q,
   if (st != DRAFT_ATTN_OK) return st;
   if (p->num_seqs == 0) return DRAFT_ATTN_OK;
   if (p->num_draft_tokens > DRAFT_ATTN_MAX_ROWS) return DRAFT_ATTN_ENOTSUP;
+  if (p->out_dtype != DRAFT_ATTN_OUT_F32) return DRAFT_ATTN_ENOTSUP;  // needs the fp32 cache result
   if (!q || !k_draft || !v_draft || !ctx_len_dev || !out || !lse) return DRAFT_ATTN_EINVAL;
   auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
   if (mis(q, 16) || mis(k_draft, 16) || mis(v_draft, 16) || mis(out, 8) || mis(lse, 4) || mis(ctx_len_dev, 4))

@@ -72,6 +72,52 @@ int32_t choose_chunk(const draft_attn_params* p, const int32_t* lens, int64_t ke
   return best;
 }
 
+// Largest number of items of one (sequence, kv head) at chunk P.
+int32_t max_group_items(const draft_attn_params* p, const int32_t* lens, int32_t P) {
+  int32_t m = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int32_t n = seq_items(seq_ranges(lens[b], p->mode, p->window, p->n_sink), P, nullptr);
+    m = n > m ? n : m;
+  }
+  return m;
+}
+
+// True when some sequence has no work item (no visible key). Its output rows
+// are written by the merge kernel only, so such a batch runs on two kernels.
+bool has_empty_group(const draft_attn_params* p, const int32_t* lens) {
+  for (int32_t b = 0; b < p->num_seqs; ++b)
+    if (seq_items(seq_ranges(lens[b], p->mode, p->window, p->n_sink), kMaxChunk, nullptr) == 0) return true;
+  return false;
+}
+
+// Smallest chunk >= lo (multiple of 32) with at most `cap` items per group;
+// -1 when even kMaxChunk has more. Group item counts do not grow with P.
+int32_t fit_group_chunk(const draft_attn_params* p, const int32_t* lens, int32_t lo, int32_t cap) {
+  if (max_group_items(p, lens, lo) <= cap) return lo;
+  if (max_group_items(p, lens, kMaxChunk) > cap) return -1;
+  int32_t bad = lo, good = kMaxChunk;
+  while (good - bad > 32) {
+    const int32_t mid = round_up_32(((int64_t)bad + good) / 2);
+    if (mid >= good) break;
+    if (max_group_items(p, lens, mid) <= cap) good = mid;
+    else bad = mid;
+  }
+  return good;
+}
+
+// Single-launch choice for DRAFT_ATTN_LAUNCH_AUTO. The single kernel saves the
+// merge kernel and one kernel boundary, but the workgroup that completes a
+// (sequence, kv head) group then merges it alone: it writes a done flag, reads
+// the group's flags and reads every partial record of the group, n items *
+// padded rows * d * 4 bytes, all through the device's coherence point. When
+// the whole step is one round of workgroups, that tail is on the critical path
+// and pays only for small groups (measured on MI355X: up to about 24 KiB of
+// records, e.g. a 256-key window at 16 rows and d = 128). When there are more
+// items than resident workgroups, early groups merge while later items still
+// stream, and it paid up to the largest group measured (160 KiB).
+constexpr size_t kAutoSingleGroupBytes = 24 * 1024;
+constexpr size_t kAutoSingleGroupBytesMultiRound = 160 * 1024;
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool finite_f(double x) { return isfinite(x) != 0; }
@@ -82,6 +128,8 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   if (!p || !out) return DRAFT_ATTN_EINVAL;
   if (p->struct_size != sizeof(draft_attn_params)) return DRAFT_ATTN_EINVAL;
   if (p->fold_variant < DRAFT_ATTN_FOLD_B || p->fold_variant > DRAFT_ATTN_FOLD_VIRTUAL) return DRAFT_ATTN_EINVAL;
+  if (p->launch < DRAFT_ATTN_LAUNCH_AUTO || p->launch > DRAFT_ATTN_LAUNCH_SINGLE) return DRAFT_ATTN_EINVAL;
+  if (p->out_dtype != DRAFT_ATTN_OUT_F32 && p->out_dtype != DRAFT_ATTN_OUT_BF16) return DRAFT_ATTN_EINVAL;
   const int32_t B = p->num_seqs, T = p->num_draft_tokens, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
   if (B < 0 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DRAFT_ATTN_EINVAL;
   if (p->block_size != kBlock) return DRAFT_ATTN_EINVAL;
@@ -125,7 +173,27 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   if (R > DRAFT_ATTN_MAX_ROWS) return DRAFT_ATTN_ENOTSUP;
 
   const int32_t row_tiles = (int32_t)((R + 15) / 16);
-  const int32_t C = p->split_keys != 0 ? p->split_keys : choose_chunk(p, ctx_len_host, keyheads, row_tiles);
+  const int32_t rows_pad = 16 * row_tiles;
+  int32_t C = p->split_keys != 0 ? p->split_keys : choose_chunk(p, ctx_len_host, keyheads, row_tiles);
+  int32_t gmax = max_group_items(p, ctx_len_host, C);
+  bool single = false;
+  if (has_empty_group(p, ctx_len_host)) {
+    single = false;
+  } else if (p->launch == DRAFT_ATTN_LAUNCH_SINGLE) {
+    single = true;
+    if (gmax > DRAFT_ATTN_MAX_GROUP_ITEMS) {
+      if (p->split_keys != 0) return DRAFT_ATTN_ENOTSUP;
+      C = fit_group_chunk(p, ctx_len_host, C, DRAFT_ATTN_MAX_GROUP_ITEMS);
+      if (C < 0) return DRAFT_ATTN_ENOTSUP;
+      gmax = max_group_items(p, ctx_len_host, C);
+    }
+  } else if (p->launch == DRAFT_ATTN_LAUNCH_AUTO) {
+    const size_t group_bytes = (size_t)gmax * rows_pad * p->head_dim * sizeof(float);
+    const int64_t slots = (int64_t)kComputeUnits * resident_per_cu(p->head_dim, row_tiles);
+    const bool multi_round = count_items(p, ctx_len_host, C) > slots;
+    single = gmax <= DRAFT_ATTN_MAX_GROUP_ITEMS &&
+             group_bytes <= (multi_round ? kAutoSingleGroupBytesMultiRound : kAutoSingleGroupBytes);
+  }
   const int64_t items = count_items(p, ctx_len_host, C);
   if (items > 0x7fffffff) return DRAFT_ATTN_EINVAL;
   if ((int64_t)B * Hkv * R > 0x7fffffff) return DRAFT_ATTN_EINVAL;
@@ -135,10 +203,15 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   out->G = G;
   out->rows = (int32_t)R;
   out->row_tiles = row_tiles;
-  out->rows_pad = 16 * out->row_tiles;
-  const size_t nrows = (size_t)items * (size_t)out->rows_pad;
-  out->stat_offset = 0;
-  out->acc_offset = align_up(nrows * 4 * sizeof(float), 256);
+  out->rows_pad = rows_pad;
+  out->single = single;
+  out->max_group_items = gmax;
+  // Layout: [one 64-bit done flag per item] [stat] [acc]. The flags are
+  // reserved on both paths so the layout does not depend on the launch shape.
+  const size_t nrows = (size_t)items * (size_t)rows_pad;
+  out->flag_offset = 0;
+  out->stat_offset = align_up((size_t)items * sizeof(uint64_t), 256);
+  out->acc_offset = out->stat_offset + align_up(nrows * 4 * sizeof(float), 256);
   out->workspace_bytes = align_up(out->acc_offset + nrows * (size_t)p->head_dim * sizeof(float), 256);
   if (out->workspace_bytes == 0) out->workspace_bytes = 256;
   return DRAFT_ATTN_OK;
@@ -200,7 +273,7 @@ int draft_attn_workspace_size(const draft_attn_params* p, const int32_t* ctx_len
 }
 
 int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t* items,
-                    int64_t capacity, int64_t* n_items, int32_t* chunk_keys) {
+                    int64_t capacity, int64_t* n_items, int32_t* chunk_keys, int32_t* launch) {
   if (!n_items || capacity < 0) return DRAFT_ATTN_EINVAL;
   da::Prepared pr;
   const int st = da::prepare(p, ctx_len_host, &pr);
@@ -222,6 +295,7 @@ int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int
   }
   *n_items = w;
   if (chunk_keys) *chunk_keys = pr.chunk;
+  if (launch) *launch = pr.single ? DRAFT_ATTN_LAUNCH_SINGLE : DRAFT_ATTN_LAUNCH_TWO_PASS;
   return DRAFT_ATTN_OK;
 }
 

@@ -16,6 +16,9 @@ struct Prepared {
   int32_t rows;           // R = G * T query rows per (sequence, kv head)
   int32_t row_tiles;      // ceil(R / 16)
   int32_t rows_pad;       // 16 * row_tiles
+  bool single;            // one kernel: a workgroup that finds its group done merges it
+  int32_t max_group_items;// largest item count of one (sequence, kv head)
+  size_t flag_offset;     // workspace offset of the per-item 64-bit done flags
   size_t stat_offset;     // workspace offset of the per-row statistics
   size_t acc_offset;      // workspace offset of the per-row partial outputs
   size_t workspace_bytes; // bytes the call needs

@@ -85,14 +85,19 @@
  *   ctx_len_host int32 [B] on the host, the same values, read for validation,
  *                grid and workspace sizing. A mismatch gives wrong results but
  *                no out-of-bounds access.
- *   out          fp32 [B][T][Hq][d], written. 8-byte aligned.
+ *   out          [B][T][Hq][d], written: fp32 (8-byte aligned) or, with
+ *                out_dtype DRAFT_ATTN_OUT_BF16, bf16 rounded to nearest even
+ *                from the fp32 result (8-byte aligned).
  *   lse          fp32 [B][T][Hq], natural log, written. 4-byte aligned.
  *   workspace    device scratch of at least draft_attn_workspace_size() bytes,
- *                256-byte aligned; its contents on entry do not matter.
+ *                256-byte aligned; its contents on entry do not matter. Its
+ *                first bytes hold one 64-bit done flag per work item for the
+ *                single-launch path; every call leaves them zero.
  *
  * Calls are asynchronous on `stream` (a hipStream_t). The library allocates
  * nothing, synchronises nothing and keeps no mutable global state: concurrent
- * calls on different streams with distinct workspaces are safe.
+ * calls on different streams with distinct workspaces are safe; calls that
+ * share a workspace must not overlap in time.
  *
  * Errors: every check runs on the host before anything is enqueued, and a
  * non-zero return means nothing was enqueued. DRAFT_ATTN_EHIP reports a launch
@@ -108,7 +113,7 @@
 extern "C" {
 #endif
 
-#define DRAFT_ATTN_ABI_VERSION 1
+#define DRAFT_ATTN_ABI_VERSION 2
 
 /* modes */
 #define DRAFT_ATTN_FULL 0
@@ -123,6 +128,17 @@ extern "C" {
 #define DRAFT_ATTN_FOLD_B 0
 #define DRAFT_ATTN_FOLD_JOINT 1
 #define DRAFT_ATTN_FOLD_VIRTUAL 2
+
+/* launch shapes (launch) */
+#define DRAFT_ATTN_LAUNCH_AUTO 0    /* the library picks one of the two below */
+#define DRAFT_ATTN_LAUNCH_TWO_PASS 1 /* streaming kernel, then a merge kernel */
+#define DRAFT_ATTN_LAUNCH_SINGLE 2  /* one kernel: a workgroup that finds every
+                                       item of its (sequence, kv head) done
+                                       merges it */
+
+/* output element types (out_dtype) */
+#define DRAFT_ATTN_OUT_F32 0
+#define DRAFT_ATTN_OUT_BF16 1
 
 /* status codes */
 #define DRAFT_ATTN_OK 0
@@ -165,7 +181,19 @@ typedef struct draft_attn_params {
   int32_t split_keys;          /* keys per work item: 0 = chosen by the library, else a
                                   multiple of 32 in [32, 65536] */
   int32_t fold_variant;        /* DRAFT_ATTN_FOLD_B (default), _JOINT or _VIRTUAL */
+  int32_t launch;              /* DRAFT_ATTN_LAUNCH_AUTO (default), _TWO_PASS or _SINGLE.
+                                  SINGLE needs at most DRAFT_ATTN_MAX_GROUP_ITEMS work
+                                  items per (sequence, kv head): with split_keys 0 the
+                                  library raises the chunk until that holds, with a
+                                  fixed split_keys the call returns DRAFT_ATTN_ENOTSUP.
+                                  A batch holding a sequence with no visible key runs
+                                  on two kernels whatever the setting (its rows are
+                                  written by the merge kernel) */
+  int32_t out_dtype;           /* DRAFT_ATTN_OUT_F32 (default) or _BF16 */
 } draft_attn_params;
+
+/* Work items one workgroup merges on the single-launch path. */
+#define DRAFT_ATTN_MAX_GROUP_ITEMS 64
 
 /* Fill *p with defaults: FULL mode, block_size 16, alpha 1, beta 0, kappa 0,
  * n0 1, NEOX with rope_theta 1e4, softmax_scale 0 (the caller sets it), all
@@ -186,16 +214,17 @@ int draft_attn_workspace_size(const draft_attn_params* p, const int32_t* ctx_len
  * when mode is DRAFT_ATTN_FOLD. Returns a DRAFT_ATTN_* status. */
 int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
                       const void* v_cache, const void* k_side, const int32_t* block_table,
-                      const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out,
+                      const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only introspection of the work decomposition a call would use: the
- * chunk size in keys (*chunk_keys) and the work items in launch order, each
- * {seq, kv_head, key_begin, key_end, partition} with partition 0 for keys read
- * from k_cache and 1 for FOLD far keys read from k_side. Writes at most
- * `capacity` items to `items` (may be NULL) and the total to *n_items. */
+ * chunk size in keys (*chunk_keys), the launch shape (*launch: _TWO_PASS or
+ * _SINGLE) and the work items in launch order, each {seq, kv_head, key_begin,
+ * key_end, partition} with partition 0 for keys read from k_cache and 1 for
+ * FOLD far keys read from k_side. Writes at most `capacity` items to `items`
+ * (may be NULL) and the total to *n_items; chunk_keys and launch may be NULL. */
 int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t* items,
-                    int64_t capacity, int64_t* n_items, int32_t* chunk_keys);
+                    int64_t capacity, int64_t* n_items, int32_t* chunk_keys, int32_t* launch);
 
 /* ---------------------------------------------------------------------------
  * Draft-token self-attention, merged into a draft_attn_decode result in place.
@@ -211,7 +240,9 @@ int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int
  * pages do not say whether the draft's own keys count).
  * q: bf16 [B][T][Hq][d] (the same queries as the decode call); k_draft (already
  * rotated at positions L_b + t) and v_draft: bf16 [B][T][Hkv][d]; out, lse: as
- * written by draft_attn_decode. p, ctx_len_dev and ctx_len_host: as for that call. */
+ * written by draft_attn_decode. p, ctx_len_dev and ctx_len_host: as for that call.
+ * The merge needs the fp32 cache result: out_dtype DRAFT_ATTN_OUT_BF16 returns
+ * DRAFT_ATTN_ENOTSUP. */
 int draft_attn_merge_draft(const draft_attn_params* p, const void* q, const void* k_draft, const void* v_draft,
                            const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out, float* lse,
                            void* stream);

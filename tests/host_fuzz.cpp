@@ -33,6 +33,8 @@ int main() {
     p.kappa = (float)pick({0, 1, -1}) * 0.1f;
     p.softmax_scale = (float)pick({0, 1}) * 0.125f;
     p.split_keys = (int)pick({0, 0, 32, 64, 48, 65536, 1 << 20});
+    p.launch = (int)pick({0, 0, 1, 2, 3, -1});
+    p.out_dtype = (int)pick({0, 0, 1, 2});
     std::vector<int32_t> lens(p.num_seqs > 0 ? p.num_seqs : 1);
     for (auto& L : lens) L = (int32_t)pick({0, 1, 15, 16, 17, 1000, 4800, 1 << 20, -3});
     size_t bytes = 0;
@@ -43,7 +45,8 @@ int main() {
     }
     int64_t n = 0;
     int32_t chunk = 0;
-    const int st2 = draft_attn_plan(&p, lens.data(), nullptr, 0, &n, &chunk);
+    int32_t launch = -1;
+    const int st2 = draft_attn_plan(&p, lens.data(), nullptr, 0, &n, &chunk, &launch);
     if (st2 != st) {
       printf("plan/workspace status mismatch %d %d\n", st, st2);
       return 1;
@@ -53,7 +56,17 @@ int main() {
     if (n > 200000) continue;
     std::vector<int32_t> items(5 * (size_t)(n > 0 ? n : 1));
     int64_t n2 = 0;
-    if (draft_attn_plan(&p, lens.data(), items.data(), n, &n2, &chunk) != DRAFT_ATTN_OK || n2 != n) return 1;
+    if (draft_attn_plan(&p, lens.data(), items.data(), n, &n2, &chunk, nullptr) != DRAFT_ATTN_OK || n2 != n) return 1;
+    if (launch != DRAFT_ATTN_LAUNCH_SINGLE && launch != DRAFT_ATTN_LAUNCH_TWO_PASS) {
+      printf("bad launch %d\n", launch);
+      return 1;
+    }
+    if (p.launch == DRAFT_ATTN_LAUNCH_TWO_PASS && launch != DRAFT_ATTN_LAUNCH_TWO_PASS) {
+      printf("two-pass request not honoured\n");
+      return 1;
+    }
+    // Single launch: every (sequence, kv head) has 1..DRAFT_ATTN_MAX_GROUP_ITEMS items.
+    std::vector<int64_t> per_group((size_t)p.num_seqs * p.num_kv_heads, 0);
     for (int64_t i = 0; i < n; ++i) {
       const int32_t* it = &items[5 * i];
       const int32_t L = lens[it[0]];
@@ -61,8 +74,15 @@ int main() {
         printf("item out of range\n");
         return 1;
       }
+      ++per_group[(size_t)it[0] * p.num_kv_heads + it[1]];
     }
-    if (bytes < (size_t)n * 16 * 4 * 4) {
+    if (launch == DRAFT_ATTN_LAUNCH_SINGLE)
+      for (int64_t c : per_group)
+        if (c < 1 || c > DRAFT_ATTN_MAX_GROUP_ITEMS) {
+          printf("single launch with %lld items in a group\n", (long long)c);
+          return 1;
+        }
+    if (bytes < (size_t)n * 8 + (size_t)n * 16 * 4 * 4) {
       printf("workspace too small for the plan\n");
       return 1;
     }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(da().LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da().lib.draft_attn_version() == 1
+    assert da().lib.draft_attn_version() == 2
 
 
 def test_params_layout_matches_the_c_compiler(tmp_path):
@@ -313,3 +313,85 @@ def test_ring_size_and_table_cover_exactly_the_touched_blocks():
     sb, rl = da().ring_size(100, 4, 7)
     with pytest.raises(da().DraftAttnError):
         da().ring_table(500, 7, 100, 4, [0] * sb, list(range(rl - 1)), 64)
+
+
+# ----------------------------------------------------------------------------- launch shape, output type
+def test_launch_and_out_dtype_validated():
+    for bad in (3, -1):
+        p = params()
+        p.launch = bad
+        assert call(p) == -1
+    p = params()
+    p.out_dtype = 2
+    assert call(p) == -1
+    p = params(out_dtype="bf16")
+    assert call(p, out=0x70002) == -1                 # bf16 out still needs 8-byte alignment
+
+
+def _group_counts(items):
+    counts = {}
+    for (b, h, _, _, _) in items:
+        counts[(b, h)] = counts.get((b, h), 0) + 1
+    return counts
+
+
+def test_single_launch_limits_items_per_group():
+    # Forced single launch with the library's chunk: the chunk grows until no
+    # (sequence, kv head) has more than MAX_GROUP_ITEMS items.
+    lens = [1 << 20, 5000]
+    p = params(num_seqs=2, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="full", launch="single",
+               max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
+    items, C = da().plan(p, lens)
+    assert da().launch_of(p, lens) == "single"
+    counts = _group_counts(items)
+    assert len(counts) == 16 and max(counts.values()) <= da().MAX_GROUP_ITEMS
+    # With a fixed chunk that leaves too many items per group, single is refused.
+    p = params(num_seqs=2, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="full", launch="single",
+               split_keys=4096, max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
+    assert call(p, lens=lens) == -4
+    # A forced two-pass launch is always honoured.
+    p = params(num_seqs=2, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="window", window=128,
+               n_sink=4, launch="two_pass", max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
+    assert da().launch_of(p, lens) == "two_pass"
+
+
+def test_batch_with_an_empty_sequence_runs_on_two_kernels():
+    for launch in ("auto", "single"):
+        p = params(launch=launch)
+        assert da().launch_of(p, [300, 0]) == "two_pass"
+        assert da().launch_of(p, [300, 17]) == "single"
+
+
+def test_auto_launch_rule():
+    # Single launch exactly when the largest group's partial records
+    # (items * padded rows * d * 4 bytes) fit in 24 KiB, or in 160 KiB when the
+    # step has more items than resident workgroups (256 compute units times 1
+    # for d = 128, 3 or 2 for d = 64 with one or two row tiles).
+    rnd = random.Random(3)
+    seen = set()
+    for _ in range(200):
+        mode = rnd.choice(["full", "window", "fold"])
+        lens = [rnd.choice([17, 300, 4096, 40000, 1 << 17]) for _ in range(rnd.randint(1, 24))]
+        T = rnd.choice([1, 2, 4, 8])
+        d = rnd.choice([64, 128])
+        Hkv = rnd.choice([2, 8])
+        p = params(num_seqs=len(lens), num_q_heads=4 * Hkv, num_kv_heads=Hkv, num_draft_tokens=T, head_dim=d,
+                   mode=mode, window=rnd.choice([16, 256, 2048, 4096]), n_sink=0 if mode == "fold" else 4,
+                   max_blocks_per_seq=(max(lens) + 15) // 16, num_blocks=1 << 14)
+        items, _ = da().plan(p, lens)
+        gmax = max(_group_counts(items).values())
+        tiles = (4 * T + 15) // 16
+        slots = 256 * (1 if d == 128 else (3 if tiles == 1 else 2))
+        cap = 160 * 1024 if len(items) > slots else 24 * 1024
+        want = "single" if gmax <= da().MAX_GROUP_ITEMS and gmax * 16 * tiles * d * 4 <= cap else "two_pass"
+        assert da().launch_of(p, lens) == want, (mode, lens, T, d)
+        seen.add((want, len(items) > slots))
+    assert len(seen) == 4, seen
+
+
+def test_merge_draft_refuses_bf16_output():
+    p = params(out_dtype="bf16")
+    host = (ctypes.c_int32 * 2)(*LENS)
+    st = da().lib.draft_attn_merge_draft(ctypes.byref(p), 0x10000, 0x20000, 0x30000, 0x60000, host, 0x70000,
+                                         0x80000, None)
+    assert st == -4

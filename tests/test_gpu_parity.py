@@ -52,7 +52,7 @@ def expected_visit(ctx_lens, stride, mode, window=0, n_sink=0, **_):
     return m
 
 
-def run_gpu(g, kw, split=0, visit=True, theta=5e5, stream=None):
+def run_gpu(g, kw, split=0, visit=True, theta=5e5, stream=None, launch="auto"):
     da = _da()
     side = g["k_side"] if kw["mode"] == "fold" else None
     vis = None
@@ -61,7 +61,7 @@ def run_gpu(g, kw, split=0, visit=True, theta=5e5, stream=None):
         vis = torch.zeros((len(g["ctx_lens"]), stride), dtype=torch.uint8, device="cuda:0")
     out, lse = da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=side,
                          ctx_lens=g["ctx_lens"], rope_theta=theta, split_keys=split, debug_visit=vis,
-                         stream=stream, **kw)
+                         stream=stream, launch=launch, **kw)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy(), (None if vis is None else vis.cpu().numpy())
 
@@ -84,9 +84,9 @@ def compare(out, lse, ref, label, pairs=None, G=None):
     assert dout <= OUT_TOL and dlse <= LSE_TOL, (label, dout, dlse)
 
 
-def check(x, kw, split=0, theta=5e5, label=""):
+def check(x, kw, split=0, theta=5e5, label="", launch="auto"):
     g = to_dev(x)
-    out, lse, vis = run_gpu(g, kw, split=split, theta=theta)
+    out, lse, vis = run_gpu(g, kw, split=split, theta=theta, launch=launch)
     n = np_inputs(x)
     ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"],
                         k_side=n["k_side"], rope_theta=theta, **kw)
@@ -104,23 +104,25 @@ def test_tiny_ctx4k_gqa4_d64_full_and_window():
         check(x, kw, theta=w.rope_theta, label=f"tiny {kw}")
 
 
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("G,T", [(4, 4), (4, 8), (1, 1), (8, 3), (2, 5)])
-def test_full_and_window_shapes(d, G, T):
+def test_full_and_window_shapes(d, G, T, launch):
     Hkv = 2
     x = synth.make_inputs(ctx_lens=[1000, 37, 4097, 16], T=T, Hq=G * Hkv, Hkv=Hkv, d=d, seed=G * 10 + T)
     for kw in (dict(mode="full"), dict(mode="window", window=300, n_sink=4),
                dict(mode="window", window=0, n_sink=7), dict(mode="window", window=2000, n_sink=0)):
-        check(x, kw, label=f"d={d} G={G} T={T} {kw}")
+        check(x, kw, label=f"d={d} G={G} T={T} {launch} {kw}", launch=launch)
 
 
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
 @pytest.mark.parametrize("rope", ["neox", "none"])
 @pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (2.0, 0.0), (4.0, -1.0), (0.5, 1.5)])
-def test_fold_modes(rope, alpha, beta):
+def test_fold_modes(rope, alpha, beta, launch):
     x = synth.make_inputs(ctx_lens=[20000, 700, 4096, 4097, 5], T=6, Hq=16, Hkv=4, d=128, seed=5,
                           fold=True, needle_frac=0.01)
     kw = dict(mode="fold", window=4096, alpha=alpha, beta=beta, rope=rope)
-    check(x, kw, label=f"fold {kw}")
+    check(x, kw, label=f"fold {launch} {kw}", launch=launch)
 
 
 def test_fold_small_window_and_zero_window():
@@ -129,21 +131,26 @@ def test_fold_small_window_and_zero_window():
         check(x, dict(mode="fold", window=W, alpha=3.0, beta=-0.5), label=f"fold W={W}")
 
 
-def test_query_scaling_batched_ragged():
-    lens = [0, 1, 17, 5000, 33333, 4096, 12000]
-    x = synth.make_inputs(ctx_lens=lens, T=4, Hq=32, Hkv=8, d=128, seed=9, fold=True)
-    for kw in (dict(mode="full", kappa=0.1, n0=4096), dict(mode="window", window=1024, n_sink=4, kappa=0.3, n0=256),
-               dict(mode="fold", window=4096, alpha=2.0, beta=0.0, kappa=0.1, n0=4096),
-               dict(mode="full", kappa=-0.05, n0=16)):
-        check(x, kw, label=f"ragged {kw}")
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
+def test_query_scaling_batched_ragged(launch):
+    # The empty sequence (L = 0) is included once; without it the batch takes
+    # the requested launch shape.
+    for lens in ([0, 1, 17, 5000, 33333, 4096, 12000], [1, 17, 5000, 33333, 4096, 12000]):
+        x = synth.make_inputs(ctx_lens=lens, T=4, Hq=32, Hkv=8, d=128, seed=9, fold=True)
+        for kw in (dict(mode="full", kappa=0.1, n0=4096),
+                   dict(mode="window", window=1024, n_sink=4, kappa=0.3, n0=256),
+                   dict(mode="fold", window=4096, alpha=2.0, beta=0.0, kappa=0.1, n0=4096),
+                   dict(mode="full", kappa=-0.05, n0=16)):
+            check(x, kw, label=f"ragged {len(lens)} seqs {launch} {kw}", launch=launch)
 
 
-@pytest.mark.parametrize("split", [32, 64, 96, 512, 4096])
-def test_split_size_sweep(split):
+@pytest.mark.parametrize("split,launch", [(32, "two_pass"), (64, "two_pass"), (96, "two_pass"), (512, "two_pass"),
+                                          (4096, "two_pass"), (160, "single"), (512, "single"), (4096, "single")])
+def test_split_size_sweep(split, launch):
     x = synth.make_inputs(ctx_lens=[9000, 333], T=4, Hq=8, Hkv=2, d=128, seed=12, fold=True)
     for kw in (dict(mode="full"), dict(mode="window", window=1000, n_sink=4),
                dict(mode="fold", window=1000, alpha=2.0, beta=-1.0)):
-        check(x, kw, split=split, label=f"split={split} {kw}")
+        check(x, kw, split=split, label=f"split={split} {launch} {kw}", launch=launch)
 
 
 def test_needles_full_attention():
@@ -265,9 +272,11 @@ def test_full_size_batch16_ragged():
         _sampled(w, kw, pairs=[(0, 2), (7, 2), (15, 6)])
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
+def test_graph_replay_matches_eager(launch):
     # The call captured in a HIP graph, replayed several times with eager work in
-    # between; every replay must equal the eager result bit for bit.
+    # between; every replay must equal the eager result bit for bit. A
+    # workspace filled with garbage before a replay must not matter.
     da = _da()
     x = synth.make_inputs(ctx_lens=[7000, 333], T=4, Hq=16, Hkv=4, d=128, seed=21, fold=True)
     g = to_dev(x)
@@ -280,7 +289,7 @@ def test_graph_replay_matches_eager():
 
     def call():
         da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=g["k_side"],
-                  ctx_lens=g["ctx_lens"], out=out, lse=lse, workspace=ws, rope_theta=5e5, **kw)
+                  ctx_lens=g["ctx_lens"], out=out, lse=lse, workspace=ws, rope_theta=5e5, launch=launch, **kw)
 
     call()
     torch.cuda.synchronize()
@@ -321,3 +330,92 @@ def test_fold_parameterisations(variant):
         ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"], k_side=n["k_side"],
                             rope_theta=5e5, fold_variant=variant, **kw)
         compare(out.cpu().numpy(), lse.cpu().numpy(), ref, f"fold variant {variant} {kw}")
+
+
+# ----------------------------------------------------------------------------- single launch, bf16 output
+def _decode(g, kw, **extra):
+    da = _da()
+    side = g["k_side"] if kw["mode"] == "fold" else None
+    out, lse = da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=side,
+                         ctx_lens=g["ctx_lens"], rope_theta=5e5, **kw, **extra)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_single_launch_reuses_one_workspace_across_shapes():
+    # Calls of different shapes share one workspace, first filled with garbage.
+    # Each must match the oracle, and each leaves its done flags at zero.
+    da = _da()
+    ws = torch.full((64 << 20,), 0x5C, dtype=torch.uint8, device="cuda:0")
+    cases = [([3000, 700, 41], 4, 16, 4, 128, dict(mode="window", window=512, n_sink=4)),
+             ([9000], 8, 32, 8, 128, dict(mode="full")),
+             ([5000, 12], 2, 8, 2, 64, dict(mode="fold", window=1000, alpha=2.0, beta=-0.5)),
+             ([3000, 700, 41], 4, 16, 4, 128, dict(mode="window", window=512, n_sink=4))]
+    for i, (lens, T, Hq, Hkv, d, kw) in enumerate(cases):
+        x = synth.make_inputs(ctx_lens=lens, T=T, Hq=Hq, Hkv=Hkv, d=d, seed=40 + i, fold=kw["mode"] == "fold")
+        g = to_dev(x)
+        out, lse = _decode(g, kw, workspace=ws, launch="single")
+        n = np_inputs(x)
+        ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"],
+                            k_side=n["k_side"], rope_theta=5e5, **kw)
+        compare(out.cpu().numpy(), lse.cpu().numpy(), ref, f"shared workspace call {i} {kw}")
+        p = da.make_params(num_seqs=len(lens), num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                           num_blocks=x["k_cache"].shape[0], max_blocks_per_seq=x["block_table"].shape[1],
+                           launch="single", **kw)
+        assert da.launch_of(p, lens) == "single"
+        n_items = len(da.plan(p, lens)[0])
+        flags = ws[:8 * n_items].cpu()
+        assert int(flags.count_nonzero()) == 0, f"call {i} left a done flag set"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_launch_at_the_group_item_limit(d):
+    # 64 items per (sequence, kv head), the most one workgroup merges, and a
+    # chunk the library raises itself to reach the limit.
+    da = _da()
+    x = synth.make_inputs(ctx_lens=[8192, 8000, 100], T=8, Hq=8, Hkv=2, d=d, seed=44, fold=True)
+    items, C = da.plan(da.make_params(num_seqs=3, num_draft_tokens=8, num_q_heads=8, num_kv_heads=2, head_dim=d,
+                                      num_blocks=x["k_cache"].shape[0], max_blocks_per_seq=x["block_table"].shape[1],
+                                      split_keys=128, launch="single"), x["ctx_lens"])
+    assert sum(1 for it in items if it[0] == 0 and it[1] == 0) == da.MAX_GROUP_ITEMS
+    for kw in (dict(mode="full"), dict(mode="fold", window=2048, alpha=3.0, beta=0.5)):
+        check(x, kw, split=128, label=f"64 items d={d} {kw}", launch="single")
+    x = synth.make_inputs(ctx_lens=[40000, 3], T=2, Hq=8, Hkv=2, d=d, seed=45)
+    check(x, dict(mode="full"), split=0, label=f"raised chunk d={d}", launch="single")
+
+
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
+def test_bf16_output(launch):
+    # bf16 output is the fp32 result of the same path rounded to nearest even,
+    # bit for bit; against the oracle the bar widens by bf16's half ulp.
+    x = synth.make_inputs(ctx_lens=[5000, 300, 17], T=4, Hq=16, Hkv=4, d=128, seed=46, fold=True,
+                          needle_frac=0.01)
+    g = to_dev(x)
+    n = np_inputs(x)
+    for kw in (dict(mode="full"), dict(mode="window", window=1000, n_sink=4),
+               dict(mode="fold", window=1000, alpha=2.0, beta=-1.0)):
+        o32, l32 = _decode(g, kw, launch=launch)
+        o16, l16 = _decode(g, kw, launch=launch, out_dtype="bf16")
+        assert o16.dtype == torch.bfloat16
+        assert torch.equal(o16, o32.to(torch.bfloat16)), f"{kw}: not the rounded fp32 result"
+        assert torch.equal(l16, l32)
+        ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"],
+                            k_side=n["k_side"], rope_theta=5e5, **kw)
+        err = np.abs(o16.float().cpu().numpy() - ref["out"])
+        bound = OUT_TOL + 2.0 ** -8 * np.abs(ref["out"])
+        print(f"bf16 {launch} {kw}: max excess {float((err - bound).max()):.3e}", flush=True)
+        assert np.all(err <= bound), kw
+
+
+def test_single_and_two_pass_agree_on_the_benchmark_shapes():
+    # Same inputs through both launch shapes at benchmark-like head counts.
+    x = synth.make_inputs(ctx_lens=[20000], T=4, Hq=32, Hkv=8, d=128, seed=47, fold=True)
+    g = to_dev(x)
+    for kw in (dict(mode="window", window=2048, n_sink=4), dict(mode="full"),
+               dict(mode="fold", window=4096, alpha=2.0, beta=-1.0, kappa=0.1, n0=4096)):
+        o1, l1 = _decode(g, kw, launch="two_pass")
+        o2, l2 = _decode(g, kw, launch="single")
+        dout = float((o1 - o2).abs().max())
+        dlse = float((l1 - l2).abs().max())
+        print(f"single vs two-pass {kw}: max|dout|={dout:.2e} max|dlse|={dlse:.2e}", flush=True)
+        assert dout <= 1e-4 and dlse <= 1e-5
