@@ -35,6 +35,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "host.h"
 #include "plan.h"
@@ -47,6 +48,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxHalfDim = 64;
+
+// Lengths and item prefix of a small batch, passed with the launch so that
+// the first dependent memory read of each workgroup (the lengths) is not
+// needed: the values arrive with the kernel arguments. nseq = 0 for larger
+// batches, whose kernels read ctx_len from device memory instead. The host
+// fills this from ctx_len_host, which the contract makes equal to ctx_len_dev.
+constexpr int kArgSeqs = 32;
+struct SeqTable {
+  int32_t nseq;                // B when B <= kArgSeqs, else 0
+  int32_t len[kArgSeqs];       // context length of each sequence
+  int32_t base[kArgSeqs + 1];  // items (over all kv heads) of the sequences before it
+};
 
 struct Pass1Args {
   const __bf16* q;
@@ -66,6 +79,7 @@ struct Pass1Args {
   int32_t mode, W, S, n0, C, rope, total_items;
   int32_t out_bf16, fold_variant;
   float alpha, kappa, scale, beta;
+  SeqTable seqs;
   double omega[kMaxHalfDim];  // RoPE frequencies rope_theta^(-2i/d)
 };
 
@@ -78,6 +92,7 @@ struct Pass2Args {
   int32_t B, T, Hq, Hkv, G, R, rows_pad;
   int32_t mode, W, S, C, total_items, fold_variant, out_bf16;
   float alpha, beta;
+  SeqTable seqs;
 };
 
 // ---------------------------------------------------------------- lane helpers
@@ -183,6 +198,29 @@ __device__ void seq_prefix(int32_t b, const int32_t* __restrict__ ctx_len, int32
   out->n_main = nm;
 }
 
+// The same two lookups from the launch's sequence table (t.nseq > 0).
+__device__ __forceinline__ bool locate_item_table(int32_t w, const SeqTable& t, int32_t mode, int32_t W, int32_t S,
+                                                  int32_t C, SeqInfo* out) {
+  if (w >= t.base[t.nseq]) return false;
+  int32_t b = 0;
+  while (b + 1 < t.nseq && w >= t.base[b + 1]) ++b;
+  int32_t nm = 0;
+  out->b = b;
+  out->base = t.base[b];
+  out->n = seq_items(seq_ranges(t.len[b], mode, W, S), C, &nm);
+  out->n_main = nm;
+  return true;
+}
+
+__device__ __forceinline__ void seq_prefix_table(int32_t b, const SeqTable& t, int32_t mode, int32_t W, int32_t S,
+                                                 int32_t C, SeqInfo* out) {
+  int32_t nm = 0;
+  out->b = b;
+  out->base = t.base[b];
+  out->n = seq_items(seq_ranges(t.len[b], mode, W, S), C, &nm);
+  out->n_main = nm;
+}
+
 // ---------------------------------------------------------------- pass 1
 // A work item (a chunk of C keys of one sequence, kv head and partition) is
 // streamed by a workgroup of kWaves waves; wave w takes the chunk's steps
@@ -193,6 +231,7 @@ constexpr int kWaves = 4;
 #ifndef DA_PREFETCH_STEPS
 #define DA_PREFETCH_STEPS 1
 #endif
+
 
 template <int D>
 struct StepRegs {
@@ -232,6 +271,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   const bool vhi = (g >> 1) != 0;    // value keys 8g..8g+7 live in the second block for g >= 2
   const bool sharp = FAR && (a.alpha != 1.f);
   const float alpha = a.alpha;
+  constexpr int PF = DA_PREFETCH_STEPS;
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -355,8 +395,8 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   };
 
   int32_t s = wave;
-  if (s < nsteps) {
-#if DA_PREFETCH_STEPS == 2
+  if (s >= nsteps) {
+  } else if constexpr (PF == 2) {
     // Loads run two of this wave's steps ahead of the compute (three buffers).
     StepRegs<D> ra, rb, rc;
     issue(s, ra);
@@ -375,7 +415,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
       s += kWaves;
       if (s >= nsteps) break;
     }
-#else
+  } else {
     // Loads run one of this wave's steps ahead of the compute (two buffers).
     StepRegs<D> ra, rb;
     issue(s, ra);
@@ -389,7 +429,6 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
       s += kWaves;
       if (s >= nsteps) break;
     }
-#endif
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -614,7 +653,9 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
   float2* s_l = (float2*)(s_m + kWaves * rp);           // [kWaves][rp] (acc denominator, plain sum)
   float* s_o = (float*)(s_l + kWaves * rp);              // [2][rp][OS] partial outputs
   SeqInfo si;
-  if (!locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si)) {
+  const bool found = a.seqs.nseq > 0 ? locate_item_table(w, a.seqs, a.mode, a.W, a.S, a.C, &si)
+                                     : locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si);
+  if (!found) {
     // Only when ctx_len on the device disagrees with the host mirror: leave a
     // neutral record so the merge stays defined.
     if (tid < a.R) a.stat[(size_t)w * rp + tid] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
@@ -622,7 +663,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
     return;
   }
   const int32_t b = si.b;
-  const int32_t L = a.ctx_len[b];
+  const int32_t L = a.seqs.nseq > 0 ? a.seqs.len[b] : a.ctx_len[b];
   const int32_t rel = w - si.base;
   const int32_t kvh = rel / si.n, kidx = rel - kvh * si.n;
   const Ranges rg = seq_ranges(L, a.mode, a.W, a.S);
@@ -829,7 +870,8 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   const int32_t kvh = bh % a.Hkv;
   const int32_t b = bh / a.Hkv;
   SeqInfo si;
-  seq_prefix(b, a.ctx_len, a.Hkv, a.mode, a.W, a.S, a.C, &si);
+  if (a.seqs.nseq > 0) seq_prefix_table(b, a.seqs, a.mode, a.W, a.S, a.C, &si);
+  else seq_prefix(b, a.ctx_len, a.Hkv, a.mode, a.W, a.S, a.C, &si);
   int64_t i0 = (int64_t)si.base + (int64_t)kvh * si.n;
   int64_t im = i0 + si.n_main;
   int64_t i1 = i0 + si.n;
@@ -1061,6 +1103,18 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a1.scale = p->softmax_scale;
   for (int i = 0; i < kMaxHalfDim; ++i)
     a1.omega[i] = i < D / 2 ? pow(p->rope_theta, -2.0 * (double)i / (double)D) : 0.0;
+  memset(&a1.seqs, 0, sizeof(a1.seqs));
+  if (p->num_seqs <= kArgSeqs) {
+    a1.seqs.nseq = p->num_seqs;
+    int32_t acc = 0;
+    for (int32_t b = 0; b < p->num_seqs; ++b) {
+      a1.seqs.len[b] = ctx_len_host[b];
+      a1.seqs.base[b] = acc;
+      acc += seq_items(seq_ranges(ctx_len_host[b], p->mode, p->window, p->n_sink), pr.chunk, nullptr) *
+             p->num_kv_heads;
+    }
+    a1.seqs.base[p->num_seqs] = acc;
+  }
 
   Pass2Args a2;
   a2.stat = a1.stat;
@@ -1084,6 +1138,7 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a2.beta = p->beta;
   a2.fold_variant = p->fold_variant;
   a2.out_bf16 = a1.out_bf16;
+  a2.seqs = a1.seqs;
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();  // clear a stale error so the check below reports ours

@@ -159,6 +159,21 @@ def test_needles_full_attention():
     check(x, dict(mode="window", window=4096, n_sink=4), label="needles window")
 
 
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
+def test_batch_above_the_argument_table(launch):
+    # Up to 32 sequences travel with the launch arguments; larger batches are
+    # located from ctx_len in device memory. 40 ragged sequences, one empty.
+    rnd = np.random.default_rng(50)
+    lens = [int(v) for v in rnd.integers(1, 3000, size=40)]
+    lens[7] = 0
+    x = synth.make_inputs(ctx_lens=lens, T=2, Hq=8, Hkv=2, d=64, seed=50, fold=True)
+    for kw in (dict(mode="full", kappa=0.1, n0=256), dict(mode="window", window=500, n_sink=4),
+               dict(mode="fold", window=700, alpha=2.0, beta=-1.0)):
+        check(x, kw, label=f"40 seqs {launch} {kw}", launch=launch)
+    x = synth.make_inputs(ctx_lens=[v if v else 5 for v in lens], T=2, Hq=8, Hkv=2, d=64, seed=51)
+    check(x, dict(mode="window", window=300, n_sink=4), label=f"40 seqs, none empty, {launch}", launch=launch)
+
+
 # ----------------------------------------------------------------------------- paging behaviour
 def test_unread_blocks_may_be_invalid():
     # Blocks wholly outside the window are never read: give them -1 table entries.
