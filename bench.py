@@ -21,8 +21,12 @@ cache -- the read that grows with context. Printed: one JSON line with
               the 8 TB/s HBM peak; traffic = FETCH_SIZE + WRITE_SIZE bytes per
               launch from rocprofv3 counters (profiles/traffic.json), when they
               were taken on the current kernel source
+  step_us_hot / step_us_cold  median, p10 and p90 of whole-call durations
+              (torch events on the call's stream), the cold ones with the 256 MB
+              Infinity Cache flushed by a 512 MiB write before each call
+  copy_ceiling  a plain 1 GiB device copy's read + write rate in the same run
   cpu_baseline  the fp64 NumPy oracle on a bounded sample of the same step,
-              timed on this host's cores
+              timed on this host's cores (BLAS threads pinned to them)
 Options select other workloads and modes for sweeps; --gpus above 1 is refused.
 """
 
@@ -167,6 +171,37 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
         for a, b in pairs:
             ev.destroy(a)
             ev.destroy(b)
+    # Whole-call durations from torch events on the call's stream: the
+    # distribution of hot steps, then cold steps with the 256 MB Infinity Cache
+    # flushed by a 512 MiB write before each call.
+    dist = cold = None
+    if want_events:
+        import statistics
+
+        def pct(v, q):
+            v = sorted(v)
+            return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            step(None)
+            b.record()
+        torch.cuda.synchronize()
+        d = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        dist = dict(median=round(statistics.median(d), 2), p10=round(pct(d, 0.1), 2), p90=round(pct(d, 0.9), 2))
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        d = []
+        for k in range(min(steps, 20)):
+            flush.fill_(k & 0xFF)
+            a, b = evs[k]
+            a.record()
+            step(None)
+            b.record()
+            torch.cuda.synchronize()
+            d.append(a.elapsed_time(b) * 1e3)
+        cold = dict(median=round(statistics.median(d), 2), p10=round(pct(d, 0.1), 2), p90=round(pct(d, 0.9), 2))
+        del flush
     ms = ms_eager
     ms_graph = None
     if graph:
@@ -193,23 +228,56 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
     keys = sum(visible_keys(L, **kw) for L in w.ctx_lens) * w.Hkv
     bytes_ = keys * 4 * w.d
     res = dict(x=x, kw=kw, ms=ms, ms_eager=ms_eager, pass1_ms=pass1, bytes=bytes_, keys=keys // w.Hkv, chunk=chunk,
-               launch=launch_used, torch_ok=bool(torch.isfinite(out).all().item()))
+               launch=launch_used, dist=dist, cold=cold, torch_ok=bool(torch.isfinite(out).all().item()))
     return res
 
 
+def copy_ceiling():
+    """Read + write rate of a plain 1 GiB device copy (torch copy_), timed with events."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    del src, dst
+    return dict(kernel="torch copy_ of 1 GiB", read_plus_write_gbs=round(2 * n / (ms * 1e-3) / 1e9, 1))
+
+
 def cpu_baseline(w, kw, x, budget_s):
-    """fp64 oracle on whole kv heads of the same step until the budget is spent."""
-    import numpy as np
+    """fp64 oracle on whole kv heads of the same step until the budget is spent, with the
+    BLAS threads pinned to this process's cores."""
+    import contextlib
 
-    import oracle
-
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        limit, threads = contextlib.nullcontext(), 1
     G = w.Hq // w.Hkv
     table = x["block_table"].cpu().numpy()
+    with limit:
+        done_bytes, spent, heads = _oracle_heads(w, kw, x, budget_s, G, table)
+    step_s = spent * w.Hkv / heads
+    return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                s_per_step=round(step_s, 3),
+                keys_per_s=round(sum(visible_keys(L, **kw) for L in w.ctx_lens) / step_s, 1),
+                sample=f"{heads} of {w.Hkv} kv heads of the same step (all {sum(w.ctx_lens)} keys each), "
+                       f"fp64 NumPy on {cores} host cores, {spent:.1f} s")
+
+
+def _oracle_heads(w, kw, x, budget_s, G, table):
+    import oracle
+
     done_bytes, spent, heads = 0, 0.0, 0
     for g in range(w.Hkv):
         q = x["q"][:, :, g * G:(g + 1) * G].float().cpu().numpy()
@@ -224,9 +292,7 @@ def cpu_baseline(w, kw, x, budget_s):
         del q, k, v, ks
         if spent >= budget_s:
             break
-    return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{heads} of {w.Hkv} kv heads of the same step (all {sum(w.ctx_lens)} keys each), "
-                       f"fp64 NumPy, {spent:.1f} s")
+    return done_bytes, spent, heads
 
 
 def traffic_for(tag):
@@ -306,6 +372,9 @@ def main():
                      "kernel": ("pass1_kernel (split-K K/V streaming)" if r["launch"] == "two_pass" else
                                 "pass1_kernel (split-K K/V streaming + in-kernel merge, single launch)"),
                      "mean_launch_ms": round(r["pass1_ms"], 5)},
+        "step_us_hot": r["dist"],
+        "step_us_cold": r["cold"],
+        "copy_ceiling": copy_ceiling() if not args.no_secondary else None,
         "secondary": secondary,
         "cpu_baseline": cpu,
     }
