@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--launch", default="auto", choices=["auto", "two_pass", "single"])
     ap.add_argument("--window", type=int, default=None, help="override the run's window (window / fold modes)")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "merge_draft"],
+                    help="decode (the hot path, default) or one of the NEXT-row kernels")
+    ap.add_argument("--case", default=None, help="append: decode | prefill; merge_draft: 1m | batch16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -306,6 +309,131 @@ def traffic_for(tag):
     return rec.get("bytes_per_launch")
 
 
+def _event_mean_us(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e6 / steps
+    return a.elapsed_time(b) * 1e3 / steps, wall
+
+
+def bench_append(args):
+    """KV append (draft_attn_append) with the FOLD side cache. Cases: 'decode' writes the
+    accepted tokens of a draft step (16 sequences x 8 tokens at ragged positions); 'prefill'
+    writes a 64K-token chunk of one sequence. Algorithmic bytes per token and kv head: read
+    k_new and v_new, write the rotated key, the side key and the value, 10 * d bytes."""
+    import numpy as np
+    import torch
+
+    import draft_attention_amd as da
+    import synth
+
+    case = args.case or "prefill"
+    Hkv, d = 8, 128
+    if case == "decode":
+        pos = synth.ragged_lengths(16, 32768, 524288, args.seed)
+        n_new = 8
+    else:
+        pos, n_new = [1000], 65536
+    B = len(pos)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    spans = [list(range(p // 16, (p + n_new - 1) // 16 + 1)) for p in pos]
+    MB = max(sp[-1] for sp in spans) + 1
+    table = torch.full((B, MB), -1, dtype=torch.int32)
+    nb = 0
+    for b, sp in enumerate(spans):
+        table[b, sp] = torch.arange(nb, nb + len(sp), dtype=torch.int32)
+        nb += len(sp)
+    table = table.to(dev)
+    kc = torch.zeros((nb, Hkv, d // 8, 16, 8), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros((nb, Hkv, d, 16), dtype=torch.bfloat16, device=dev)
+    ks = torch.zeros_like(kc)
+    kn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    posd = torch.tensor(pos, dtype=torch.int32, device=dev)
+
+    def call():
+        da.append(kn, vn, table, posd, kc, vc, ks, rope="neox", rope_theta=5e5, pos_host=pos)
+
+    us, wall = _event_mean_us(call, args.steps, args.warmup)
+    nbytes = B * n_new * Hkv * 10 * d
+    gbs = nbytes / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nb_s = min(B, 2) if case == "decode" else 1
+        ns = n_new if case == "decode" else 4096
+        kn_s, vn_s = kn[:nb_s, :ns].double().cpu().numpy(), vn[:nb_s, :ns].double().cpu().numpy()
+        top = max(int(table[b, (pos[b] + ns - 1) // 16]) for b in range(nb_s)) + 1   # blocks the sample touches
+        pools = [t[:top].double().cpu().numpy() for t in (kc, vc, ks)]
+        t0 = time.perf_counter()
+        oracle.append(kn_s, vn_s, table[:nb_s].cpu().numpy(), pos[:nb_s], *pools, rope="neox", rope_theta=5e5)
+        spent = time.perf_counter() - t0
+        cpu = dict(value=round(nb_s * ns * Hkv * 10 * d / spent / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                   sample=f"{nb_s} sequence(s) x {ns} tokens x {Hkv} kv heads, fp64 NumPy, {spent:.2f} s")
+    line = {"metric": "KV append GB/s (rotated key + side key + value writes)", "value": round(gbs, 2),
+            "unit": "GB/s", "op": "append", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "us_per_call": round(us, 2), "us_per_call_wall": round(wall, 2), "higher_is_better": True,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"case": case, "num_seqs": B, "num_new": n_new, "kv_heads": Hkv, "head_dim": d,
+                       "side_cache": True, "positions": pos if B <= 4 else f"{B} ragged"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "append_kernel",
+                         "bytes_per_launch": nbytes},
+            "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+def bench_merge_draft(args):
+    """Draft-token self-attention merged into a decode result (draft_attn_merge_draft).
+    Cases: '1m' (1 sequence, 8 draft tokens, 32/8 heads) and 'batch16' (16 sequences, 4
+    draft tokens). Algorithmic bytes: q, the draft keys and values, out and lse read and
+    written once."""
+    import torch
+
+    import draft_attention_amd as da
+
+    case = args.case or "1m"
+    B, T = (1, 8) if case == "1m" else (16, 4)
+    Hq, Hkv, d = 32, 8, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    q = torch.randn((B, T, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    kd = torch.randn((B, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vd = torch.randn((B, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.randn((B, T, Hq, d), generator=g, device=dev)
+    lse = torch.randn((B, T, Hq), generator=g, device=dev)
+    lens = [1 << 20] * B if case == "1m" else [100000 + 1000 * b for b in range(B)]
+    ctx = torch.tensor(lens, dtype=torch.int32, device=dev)
+
+    def call():
+        da.merge_draft(q, kd, vd, ctx, out, lse, num_blocks=1 << 17, max_blocks_per_seq=1 << 16,
+                       num_kv_heads=Hkv, ctx_lens=lens)
+
+    us, wall = _event_mean_us(call, args.steps, args.warmup)
+    nbytes = B * T * (Hq * d * 2 + 2 * Hkv * d * 2 + 2 * Hq * d * 4 + 2 * Hq * 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    line = {"metric": "draft self-attention merge: us per call", "value": round(us, 2), "unit": "us",
+            "op": "merge_draft", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "us_per_call_wall": round(wall, 2), "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"case": case, "num_seqs": B, "draft_tokens": T, "q_heads": Hq, "kv_heads": Hkv,
+                       "head_dim": d},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None, "kernel": "merge_draft_kernel",
+                         "bytes_per_launch": nbytes, "note": "a few hundred KB per call: launch- and latency-bound"},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -315,6 +443,12 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
+        return
+    if args.op == "append":
+        bench_append(args)
+        return
+    if args.op == "merge_draft":
+        bench_merge_draft(args)
         return
     import synth
 

@@ -6,8 +6,10 @@
 // at position p this kernel writes the key turned to its own position, R(p) k,
 // into k_cache, the unrotated key into k_side, and the value into v_cache, at the
 // slot the block table gives for p. The rotation is done in fp64 (angles formed
-// and reduced by the fp64 sincos) and rounded once to bf16, to nearest with ties
-// to even, so the stored key is the correctly rounded value of the exact rotation.
+// and reduced by the fp64 sincos, then advanced by fp64 rotation steps across a
+// few consecutive positions) and rounded once to bf16, to nearest with ties to
+// even: the stored key is the bf16 value nearest to an fp64 rotation that is
+// within a few fp64 ulps of the exact one.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -16,8 +18,6 @@
 
 namespace da {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 struct AppendArgs {
   const __bf16* k_new;  // [B][n_new][Hkv][D]
@@ -28,7 +28,10 @@ struct AppendArgs {
   __bf16* v;            // [blocks][Hkv][D][16]
   __bf16* ks;           // like k, or null
   int32_t B, n_new, Hkv, max_blocks, num_blocks, rope;
+  int32_t span;         // logical blocks one sequence's append can touch
   double omega[64];     // rope_theta^(-2i/D)
+  double cos_w[64];     // cos(omega_i), sin(omega_i): one position step
+  double sin_w[64];
 };
 
 // fp64 -> bf16 bits, round to nearest, ties to even, for finite values in the
@@ -43,61 +46,100 @@ __device__ __forceinline__ unsigned short bf16_bits_rne(double x) {
   return (unsigned short)(__float_as_uint(f) >> 16);
 }
 
-// One thread per (sequence, new token, kv head, channel octet c < D/16): it owns
-// channels 8c..8c+7 and their rotation partners 8c+D/2..8c+D/2+7.
+// One workgroup per (sequence, logical block, kv head) that the append touches;
+// it owns the new tokens of that block, slots s0 .. s1-1. They are staged in LDS
+// with row-contiguous loads, rotated there, and written back as whole 16-byte
+// runs of each cache layout: 16 slots of one key octet for k_cache and k_side,
+// 8 slots of one channel for v_cache (a partial run at the edges of the append
+// is written per slot). Rotation: thread (pair i, slot group q) forms the angle
+// of its first slot with the fp64 sincos and advances it one position at a time
+// by the rotation (cos w_i, sin w_i), which adds a few fp64 ulps.
 template <int D>
 __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
-  constexpr int NC = D / 16;
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.n_new * a.Hkv * NC;
-  if (t >= total) return;
-  const int32_t c = (int32_t)(t % NC);
-  t /= NC;
-  const int32_t h = (int32_t)(t % a.Hkv);
-  t /= a.Hkv;
-  const int32_t i = (int32_t)(t % a.n_new);
-  const int32_t b = (int32_t)(t / a.n_new);
-  const int32_t p = a.pos[b] + i;
-  if (p < 0 || (p >> 4) >= a.max_blocks) return;
-  const int32_t id = a.table[(int64_t)b * a.max_blocks + (p >> 4)];
+  constexpr int NO = D / 8;               // channel octets
+  constexpr int HALF = D / 2;             // rotation pairs
+  constexpr int SPT = 16 * HALF / 256;    // slots per thread in the rotation
+  constexpr int LD = D + 8;               // padded LDS row (elements)
+  __shared__ __align__(16) __bf16 s_k[16][LD];
+  __shared__ __align__(16) __bf16 s_v[16][LD];
+  __shared__ __align__(16) __bf16 s_r[16][LD];
+  const int tid = threadIdx.x;
+  int64_t w = blockIdx.x;
+  const int32_t h = (int32_t)(w % a.Hkv);
+  w /= a.Hkv;
+  const int32_t jj = (int32_t)(w % a.span);
+  const int32_t b = (int32_t)(w / a.span);
+  const int32_t p0 = a.pos[b];
+  if (p0 < 0) return;
+  const int32_t j = (p0 >> 4) + jj;
+  const int64_t lo64 = (int64_t)j * 16 > p0 ? (int64_t)j * 16 : p0;
+  const int64_t hi64 = (int64_t)p0 + a.n_new < (int64_t)j * 16 + 16 ? (int64_t)p0 + a.n_new : (int64_t)j * 16 + 16;
+  if (lo64 >= hi64 || j >= a.max_blocks) return;
+  const int32_t id = a.table[(int64_t)b * a.max_blocks + j];
   if (id < 0 || id >= a.num_blocks) return;  // no block allocated: nothing is written
-  const int32_t slot = p & 15;
+  const int s0 = (int)(lo64 - (int64_t)j * 16), s1 = (int)(hi64 - (int64_t)j * 16);
+  const int32_t i0 = (int32_t)(lo64 - p0);  // index of slot s0's token among the new ones
 
-  const size_t src = (((size_t)b * a.n_new + i) * a.Hkv + h) * D;
-  const bf16x8 x1 = *(const bf16x8*)(a.k_new + src + 8 * c);
-  const bf16x8 x2 = *(const bf16x8*)(a.k_new + src + 8 * c + D / 2);
-  const bf16x8 v1 = *(const bf16x8*)(a.v_new + src + 8 * c);
-  const bf16x8 v2 = *(const bf16x8*)(a.v_new + src + 8 * c + D / 2);
-
-  const size_t blk = ((size_t)id * a.Hkv + h) * (size_t)(D * 16);
-  const size_t k_lo = blk + ((size_t)c * 16 + slot) * 8;              // channel octet c
-  const size_t k_hi = blk + ((size_t)(c + D / 16) * 16 + slot) * 8;   // octet c + D/16
-  if (a.ks != nullptr) {
-    *(bf16x8*)(a.ks + k_lo) = x1;
-    *(bf16x8*)(a.ks + k_hi) = x2;
+  // Stage the new tokens' keys and values: one 16-byte octet per thread.
+  for (int e = tid; e < 16 * NO; e += 256) {
+    const int s = e / NO, c = e - s * NO;
+    if (s < s0 || s >= s1) continue;
+    const size_t src = (((size_t)b * a.n_new + (i0 + s - s0)) * a.Hkv + h) * D + 8 * c;
+    *(uint4*)&s_k[s][8 * c] = *(const uint4*)(a.k_new + src);
+    *(uint4*)&s_v[s][8 * c] = *(const uint4*)(a.v_new + src);
   }
+  __syncthreads();
+
+  // Rotate: thread (i, q) owns pair (i, i + D/2) of slots q*SPT .. q*SPT + SPT - 1.
   if (a.rope == DRAFT_ATTN_ROPE_NEOX) {
-    u16x8 r1, r2;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    const int i = tid % HALF, q = tid / HALF;
+    int sa = q * SPT, sb = sa + SPT;
+    sa = sa > s0 ? sa : s0;
+    sb = sb < s1 ? sb : s1;
+    if (sa < sb) {
       double sn, cs;
-      sincos((double)p * a.omega[8 * c + e], &sn, &cs);
-      const double y1 = (double)(float)x1[e] * cs - (double)(float)x2[e] * sn;
-      const double y2 = (double)(float)x1[e] * sn + (double)(float)x2[e] * cs;
-      r1[e] = bf16_bits_rne(y1);
-      r2[e] = bf16_bits_rne(y2);
+      sincos((double)((int64_t)j * 16 + sa) * a.omega[i], &sn, &cs);
+      const double cw = a.cos_w[i], sw = a.sin_w[i];
+      for (int s = sa; s < sb; ++s) {
+        const double x1 = (double)(float)s_k[s][i], x2 = (double)(float)s_k[s][i + HALF];
+        const unsigned short r1 = bf16_bits_rne(x1 * cs - x2 * sn);
+        const unsigned short r2 = bf16_bits_rne(x1 * sn + x2 * cs);
+        s_r[s][i] = __builtin_bit_cast(__bf16, r1);
+        s_r[s][i + HALF] = __builtin_bit_cast(__bf16, r2);
+        const double c2 = cs * cw - sn * sw;
+        sn = sn * cw + cs * sw;
+        cs = c2;
+      }
     }
-    *(u16x8*)(a.k + k_lo) = r1;
-    *(u16x8*)(a.k + k_hi) = r2;
-  } else {
-    *(bf16x8*)(a.k + k_lo) = x1;
-    *(bf16x8*)(a.k + k_hi) = x2;
   }
-  // Values: channel-major blocks, one 2-byte store per channel.
+  __syncthreads();
+  const __bf16(*kr)[LD] = a.rope == DRAFT_ATTN_ROPE_NEOX ? s_r : s_k;
+
+  // Keys: thread (octet c, slot s) writes 16 bytes at [c][s]; 16 consecutive
+  // threads cover one octet's 256 contiguous bytes.
+  const size_t blk = ((size_t)id * a.Hkv + h) * (size_t)(D * 16);
+  for (int e = tid; e < 16 * NO; e += 256) {
+    const int c = e / 16, s = e - c * 16;
+    if (s < s0 || s >= s1) continue;
+    const size_t dst = blk + ((size_t)c * 16 + s) * 8;
+    *(uint4*)(a.k + dst) = *(const uint4*)&kr[s][8 * c];
+    if (a.ks != nullptr) *(uint4*)(a.ks + dst) = *(const uint4*)&s_k[s][8 * c];
+  }
+  // Values: thread (channel ch, half g) writes slots 8g .. 8g+7 of channel ch.
+  for (int e = tid; e < 2 * D; e += 256) {
+    const int ch = e >> 1, g = e & 1;
+    const int sa = 8 * g, sb = sa + 8;
+    __bf16* dst = a.v + blk + (size_t)ch * 16 + sa;
+    if (sa >= s0 && sb <= s1) {
+      typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+      bf16x8_t o;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a.v[blk + (size_t)(8 * c + e) * 16 + slot] = v1[e];
-    a.v[blk + (size_t)(8 * c + e + D / 2) * 16 + slot] = v2[e];
+      for (int k = 0; k < 8; ++k) o[k] = s_v[sa + k][ch];
+      *(bf16x8_t*)dst = o;
+    } else {
+      for (int k = 0; k < 8; ++k)
+        if (sa + k >= s0 && sa + k < s1) dst[k] = s_v[sa + k][ch];
+    }
   }
 }
 
@@ -130,9 +172,13 @@ extern "C" int draft_attn_append(const draft_attn_append_params* p, const void* 
   a.num_blocks = p->num_blocks;
   a.rope = p->rope;
   const int D = p->head_dim;
-  for (int i = 0; i < 64; ++i) a.omega[i] = i < D / 2 ? pow(p->rope_theta, -2.0 * (double)i / (double)D) : 0.0;
-  const int64_t threads = (int64_t)a.B * a.n_new * a.Hkv * (D / 16);
-  const uint32_t grid = (uint32_t)((threads + 255) / 256);
+  for (int i = 0; i < 64; ++i) {
+    a.omega[i] = i < D / 2 && p->rope == DRAFT_ATTN_ROPE_NEOX ? pow(p->rope_theta, -2.0 * (double)i / (double)D) : 0.0;
+    a.cos_w[i] = cos(a.omega[i]);
+    a.sin_w[i] = sin(a.omega[i]);
+  }
+  a.span = (p->num_new + 15) / 16 + 1;
+  const uint32_t grid = (uint32_t)((int64_t)a.B * a.span * a.Hkv);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (D == 64) append_kernel<64><<<grid, 256, 0, s>>>(a);

@@ -230,7 +230,8 @@ int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host) {
     if ((int64_t)pos_host[b] + p->num_new > (int64_t)p->max_blocks_per_seq * kBlock) return DRAFT_ATTN_EINVAL;
   }
   if (p->head_dim != 64 && p->head_dim != 128) return DRAFT_ATTN_ENOTSUP;
-  if ((int64_t)p->num_seqs * p->num_new * p->num_kv_heads * (p->head_dim / 16) > (int64_t)0x7fffffff * 256)
+  // grid: one workgroup per (sequence, touched logical block, kv head)
+  if ((int64_t)p->num_seqs * ((p->num_new + 15) / 16 + 1) * p->num_kv_heads > (int64_t)0x7fffffff)
     return DRAFT_ATTN_EINVAL;
   return DRAFT_ATTN_OK;
 }
