@@ -361,8 +361,7 @@ def bench_append(args):
     vn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
     posd = torch.tensor(pos, dtype=torch.int32, device=dev)
 
-    def call():
-        da.append(kn, vn, table, posd, kc, vc, ks, rope="neox", rope_theta=5e5, pos_host=pos)
+    call = da.prepare_append(kn, vn, table, posd, kc, vc, ks, rope="neox", rope_theta=5e5, pos_host=pos)
 
     us, wall = _event_mean_us(call, args.steps, args.warmup)
     nbytes = B * n_new * Hkv * 10 * d
@@ -415,9 +414,8 @@ def bench_merge_draft(args):
     lens = [1 << 20] * B if case == "1m" else [100000 + 1000 * b for b in range(B)]
     ctx = torch.tensor(lens, dtype=torch.int32, device=dev)
 
-    def call():
-        da.merge_draft(q, kd, vd, ctx, out, lse, num_blocks=1 << 17, max_blocks_per_seq=1 << 16,
-                       num_kv_heads=Hkv, ctx_lens=lens)
+    call = da.prepare_merge_draft(q, kd, vd, ctx, out, lse, num_blocks=1 << 17, max_blocks_per_seq=1 << 16,
+                                  num_kv_heads=Hkv, ctx_lens=lens)
 
     us, wall = _event_mean_us(call, args.steps, args.warmup)
     nbytes = B * T * (Hq * d * 2 + 2 * Hkv * d * 2 + 2 * Hq * d * 4 + 2 * Hq * 4)

@@ -363,6 +363,60 @@ def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, *, rop
         raise DraftAttnError(st, "draft_attn_append")
 
 
+class PreparedCall:
+    """A library call with its arguments marshalled once; calling it enqueues the call again
+    (on the stream given at preparation, or on `stream`)."""
+
+    def __init__(self, fn, name, params, args, keep, result=None):
+        self._fn, self._name, self.params, self.args, self._keep, self._result = fn, name, params, args, keep, result
+
+    def __call__(self, stream=None):
+        args = self.args if stream is None else self.args[:-1] + (int(stream),)
+        st = self._fn(ctypes.byref(self.params), *args)
+        if st != OK:
+            raise DraftAttnError(st, self._name)
+        return self._result
+
+
+def prepare_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, *, rope="neox", rope_theta=1e4,
+                   pos_host=None, stream=None) -> PreparedCall:
+    """Marshal the arguments of append() once (same meaning as there)."""
+    import torch
+
+    B, n_new, Hkv, d = k_new.shape
+    if pos_host is None:
+        pos_host = [int(x) for x in pos.cpu().tolist()]
+    p = make_append_params(num_seqs=B, num_new=n_new, num_kv_heads=Hkv, head_dim=d, num_blocks=k_cache.shape[0],
+                           max_blocks_per_seq=block_table.shape[1], rope=rope, rope_theta=rope_theta)
+    s = torch.cuda.current_stream(k_new.device).cuda_stream if stream is None else int(stream)
+    host = _host_i32(pos_host)
+    args = (k_new.data_ptr(), v_new.data_ptr(), block_table.data_ptr(), pos.data_ptr(), host, k_cache.data_ptr(),
+            v_cache.data_ptr(), None if k_side is None else k_side.data_ptr(), s)
+    keep = (k_new, v_new, block_table, pos, k_cache, v_cache, k_side, host)
+    return PreparedCall(lib.draft_attn_append, "draft_attn_append", p, args, keep)
+
+
+def prepare_merge_draft(q, k_draft, v_draft, ctx_len, out, lse, *, num_blocks, max_blocks_per_seq, num_kv_heads,
+                        mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0, n0=1, softmax_scale=None,
+                        rope="neox", rope_theta=1e4, ctx_lens=None, stream=None) -> PreparedCall:
+    """Marshal the arguments of merge_draft() once (same meaning as there)."""
+    import torch
+
+    B, T, Hq, d = q.shape
+    if ctx_lens is None:
+        ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
+    p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=num_kv_heads, head_dim=d,
+                    num_blocks=num_blocks, max_blocks_per_seq=max_blocks_per_seq, mode=mode, window=window,
+                    n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0, softmax_scale=softmax_scale,
+                    rope=rope, rope_theta=rope_theta)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
+    host = _host_i32(ctx_lens)
+    args = (q.data_ptr(), k_draft.data_ptr(), v_draft.data_ptr(), ctx_len.data_ptr(), host, out.data_ptr(),
+            lse.data_ptr(), s)
+    keep = (q, k_draft, v_draft, ctx_len, out, lse, host)
+    return PreparedCall(lib.draft_attn_merge_draft, "draft_attn_merge_draft", p, args, keep, (out, lse))
+
+
 def merge_draft(q, k_draft, v_draft, ctx_len, out, lse, *, num_blocks, max_blocks_per_seq, num_kv_heads,
                 mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0, n0=1, softmax_scale=None,
                 rope="neox", rope_theta=1e4, ctx_lens=None, stream=None):

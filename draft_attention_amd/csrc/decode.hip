@@ -548,9 +548,12 @@ __device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int3
       const int prow = pair / NQ, q4 = pair - prow * NQ;
 #pragma unroll
       for (int k = 0; k < IB; ++k) {
+        // unconditional load from a clamped index (see the merge kernel)
         const int32_t it = ib + k;
-        v[j][k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (prow < a.R && it < n) v[j][k] = load_dev4(a.acc + ((size_t)(i0 + it) * rp + prow) * D + 4 * q4);
+        const bool ok = prow < a.R && it < n;
+        const int32_t itc = it < n ? it : n - 1, prc = prow < a.R ? prow : a.R - 1;
+        const float4 x = load_dev4(a.acc + ((size_t)(i0 + itc) * rp + prc) * D + 4 * q4);
+        v[j][k] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   };
@@ -560,8 +563,9 @@ __device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int3
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const int it = sub + 8 * k;
-    st[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-    if (row_ok && it < n) st[k] = load_dev4((const float*)&a.stat[(size_t)(i0 + it) * rp + row]);
+    const int itc = it < n ? it : n - 1, rc = row_ok ? row : a.R - 1;
+    const float4 x = load_dev4((const float*)&a.stat[(size_t)(i0 + itc) * rp + rc]);
+    st[k] = row_ok && it < n ? x : make_float4(-INFINITY, 0.f, 0.f, 0.f);
   }
   float M = -INFINITY, MF = -INFINITY;
 #pragma unroll
@@ -690,7 +694,8 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
       bf16x8 z;
 #pragma unroll
       for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
-      qh[rt][ks] = ok ? *(const bf16x8*)(qp + 32 * ks) : z;
+      const bf16x8 qv = *(const bf16x8*)(qp + 32 * ks);  // qp is a valid row even when !ok
+      qh[rt][ks] = ok ? qv : z;
       ql[rt][ks] = z;
     }
   }
@@ -915,30 +920,43 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   float M, MF, Ls, ZF, ZFa;
   float4 accp[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
   if (n <= (int64_t)NG * kFastItems) {
-    // one round of loads
+    // One round of loads. Each load reads a valid record (its index clamped to
+    // the row's last item) and its value always enters the arithmetic: out of
+    // range, a statistic gets -inf added and a partial output a zero weight.
+    // A value used only under a condition lets the compiler move its load into
+    // the branch and wait for it there, which would serialise the round.
     const bool has_st = tid < n;
-    float4 st = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-    if (has_st) st = a.stat[(size_t)(i0 + tid) * rp + row];
+    const int64_t nl = n > 0 ? n - 1 : 0;  // n == 0: nothing is read
     float4 v[kFastItems];
+    float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (n > 0) {
 #pragma unroll
-    for (int k = 0; k < kFastItems; ++k) {
-      const int64_t i = grp + (int64_t)k * NG;
-      v[k] = i < n ? *(const float4*)(accrow + (size_t)(i0 + i) * rp * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < kFastItems; ++k) {
+        const int64_t i = grp + (int64_t)k * NG;
+        v[k] = *(const float4*)(accrow + (size_t)(i0 + (i < n ? i : nl)) * rp * D);
+      }
+      sv = a.stat[(size_t)(i0 + (has_st ? tid : nl)) * rp + row];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFastItems; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const float st_m = sv.x + (has_st ? 0.f : -INFINITY);  // record max (log2), -inf if none
+    const float st_y = sv.y * (has_st ? 1.f : 0.f);
+    const float st_z = sv.z * (has_st ? 1.f : 0.f);
     const bool is_main = i0 + tid < im;
-    M = has_st && is_main ? st.x : -INFINITY;
-    MF = has_st && !is_main ? st.x : -INFINITY;
+    M = is_main ? st_m : -INFINITY;
+    MF = is_main ? -INFINITY : st_m;
     block_max2(M, MF);
     float sc = 0.f;
     Ls = 0.f; ZF = 0.f; ZFa = 0.f;
-    if (has_st && st.x != -INFINITY) {
+    if (st_m != -INFINITY) {
       if (is_main) {
-        sc = exp2f(st.x - M);
-        Ls = st.y * sc;
+        sc = exp2f(st_m - M);
+        Ls = st_y * sc;
       } else {
-        sc = exp2f(alpha * (st.x - MF));
-        ZF = st.z * exp2f(st.x - MF);
-        ZFa = st.y * sc;
+        sc = exp2f(alpha * (st_m - MF));
+        ZF = st_z * exp2f(st_m - MF);
+        ZFa = st_y * sc;
       }
     }
     if (tid < n) s_scale[tid] = sc;
@@ -946,14 +964,17 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
 #pragma unroll
     for (int k = 0; k < kFastItems; ++k) {
       const int64_t i = grp + (int64_t)k * NG;
-      if (i < n) {
-        const float sk = s_scale[i];
-        float4& acc = (i0 + i < im) ? accp[0] : accp[1];
-        acc.x += sk * v[k].x;
-        acc.y += sk * v[k].y;
-        acc.z += sk * v[k].z;
-        acc.w += sk * v[k].w;
-      }
+      const bool ok = i < n;
+      const float sk = s_scale[ok ? i : 0] * (ok ? 1.f : 0.f);
+      const float wm = i0 + i < im ? sk : 0.f, wf = i0 + i < im ? 0.f : sk;
+      accp[0].x += wm * v[k].x;
+      accp[0].y += wm * v[k].y;
+      accp[0].z += wm * v[k].z;
+      accp[0].w += wm * v[k].w;
+      accp[1].x += wf * v[k].x;
+      accp[1].y += wf * v[k].y;
+      accp[1].z += wf * v[k].z;
+      accp[1].w += wf * v[k].w;
     }
   } else {
     // long rows: maxima, sums, then the partial outputs tile by tile

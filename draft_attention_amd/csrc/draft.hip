@@ -38,57 +38,79 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // One wave per (sequence, draft token, query head); lane l owns channels
-// l*CPL .. l*CPL + CPL - 1.
-template <int D>
+// l*CPL .. l*CPL + CPL - 1. Every load the wave needs (its query row, the cache
+// result, draft keys and values 0..t) is issued before any is used, so the call
+// costs about one memory round trip; the logits are then reduced across the
+// wave one draft key at a time.
+template <int D, int TM>
 __global__ __launch_bounds__(64) void merge_draft_kernel(const MergeArgs a) {
   constexpr int CPL = D / 64;
   const int lane = threadIdx.x;
-  int64_t r = blockIdx.x;
-  const int32_t h = (int32_t)(r % a.Hq);
-  r /= a.Hq;
-  const int32_t t = (int32_t)(r % a.T);
-  const int32_t b = (int32_t)(r / a.T);
+  uint32_t r = blockIdx.x;  // grid = B * T * Hq < 2^31, checked on the host
+  const int32_t h = (int32_t)(r % (uint32_t)a.Hq);
+  r /= (uint32_t)a.Hq;
+  const int32_t t = (int32_t)(r % (uint32_t)a.T);
+  const int32_t b = (int32_t)(r / (uint32_t)a.T);
   const int32_t kvh = h / a.G;
+  const int64_t qrow = ((int64_t)b * a.T + t) * a.Hq + h;
+
+  float qv[CPL], oc[CPL];
+  float kx[TM][CPL], vx[TM][CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    qv[e] = (float)a.q[qrow * D + lane * CPL + e];
+    oc[e] = a.out[qrow * D + lane * CPL + e];
+  }
+  const float lse_c = a.lse[qrow];
+  // Loads are unconditional, from row min(j, t): a load under a condition makes
+  // the compiler wait for it before the branch joins.
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int32_t jc = j <= t ? j : t;
+    const int64_t row = (((int64_t)b * a.T + jc) * a.Hkv + kvh) * D + lane * CPL;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      kx[j][e] = (float)a.kd[row + e];
+      vx[j][e] = (float)a.vd[row + e];
+    }
+  }
   const int32_t n = visible_count(a.ctx_len[b], a.mode, a.W, a.S);
   const double sn = 1.0 + (double)a.kappa * log((double)(n > a.n0 ? n : a.n0) / (double)a.n0);
   const float c = (float)((double)a.scale * sn);
 
-  const int64_t qrow = ((int64_t)b * a.T + t) * a.Hq + h;
-  float qv[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) qv[j] = (float)a.q[qrow * D + lane * CPL + j];
-
-  // Logits of draft keys 0..t as wave-reduced dot products: one pass for the
-  // maximum, a second (recomputing them) for the sums.
-  auto logit = [&](int32_t j) {
-    const __bf16* kr = a.kd + (((int64_t)b * a.T + j) * a.Hkv + kvh) * D + lane * CPL;
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) part += qv[e] * (float)kr[e];
-    return c * wave_sum(part);
-  };
+  float lg[TM];
   float m = -INFINITY;
-  for (int32_t j = 0; j <= t; ++j) m = fmaxf(m, logit(j));
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    lg[j] = -INFINITY;
+    if (j <= t) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) part += qv[e] * kx[j][e];
+      lg[j] = c * wave_sum(part);
+      m = fmaxf(m, lg[j]);
+    }
+  }
   float z = 0.f, od[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) od[e] = 0.f;
-  for (int32_t j = 0; j <= t; ++j) {
-    const float pj = expf(logit(j) - m);
-    z += pj;
-    const __bf16* vr = a.vd + (((int64_t)b * a.T + j) * a.Hkv + kvh) * D + lane * CPL;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) od[e] += pj * (float)vr[e];
+  for (int j = 0; j < TM; ++j) {
+    if (j <= t) {
+      const float pj = expf(lg[j] - m);
+      z += pj;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) od[e] += pj * vx[j][e];
+    }
   }
   const float lse_d = m + logf(z);
-  const float lse_c = a.lse[qrow];
   const float top = fmaxf(lse_c, lse_d);
   const float wc = expf(lse_c - top), wd = expf(lse_d - top);
   const float den = wc + wd;
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
-    float* o = a.out + qrow * D + lane * CPL + e;
-    const float oc = wc > 0.f ? *o : 0.f;
-    *o = (wc * oc + wd * od[e] / z) / den;
+    const float o = wc > 0.f ? oc[e] : 0.f;
+    a.out[qrow * D + lane * CPL + e] = (wc * o + wd * od[e] / z) / den;
   }
   if (lane == 0) a.lse[qrow] = top + logf(den);
 }
@@ -127,11 +149,21 @@ extern "C" int draft_attn_merge_draft(const draft_attn_params* p, const void* q,
   a.n0 = p->n0;
   a.kappa = p->kappa;
   a.scale = p->softmax_scale;
+  if ((int64_t)a.B * a.T * a.Hq > 0x7fffffff) return DRAFT_ATTN_EINVAL;
   const uint32_t grid = (uint32_t)((int64_t)a.B * a.T * a.Hq);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  if (p->head_dim == 64) merge_draft_kernel<64><<<grid, 64, 0, s>>>(a);
-  else merge_draft_kernel<128><<<grid, 64, 0, s>>>(a);
+  // The kernel holds draft keys 0..TM-1 in registers: TM is the smallest of 8,
+  // 16 and 32 that covers T.
+  if (p->head_dim == 64) {
+    if (a.T <= 8) merge_draft_kernel<64, 8><<<grid, 64, 0, s>>>(a);
+    else if (a.T <= 16) merge_draft_kernel<64, 16><<<grid, 64, 0, s>>>(a);
+    else merge_draft_kernel<64, 32><<<grid, 64, 0, s>>>(a);
+  } else {
+    if (a.T <= 8) merge_draft_kernel<128, 8><<<grid, 64, 0, s>>>(a);
+    else if (a.T <= 16) merge_draft_kernel<128, 16><<<grid, 64, 0, s>>>(a);
+    else merge_draft_kernel<128, 32><<<grid, 64, 0, s>>>(a);
+  }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
 }

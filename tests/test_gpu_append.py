@@ -130,3 +130,22 @@ def test_cache_built_by_appends_then_decoded():
         dlse = float(np.abs(lse.cpu().numpy() - ref["lse"]).max())
         print(f"appended cache {kw}: max|dout|={dout:.3e} max|dlse|={dlse:.3e}", flush=True)
         assert dout <= 1e-2 and dlse <= 1e-3
+
+
+def test_prepared_append_matches_the_direct_call():
+    da = _da()
+    dev = torch.device("cuda:0")
+    lens = [40, 3]
+    x = synth.make_inputs(ctx_lens=[L + 37 for L in lens], T=1, Hq=2, Hkv=2, d=128, seed=33, fold=True)
+    g = torch.Generator().manual_seed(8)
+    kn = torch.randn((2, 37, 2, 128), generator=g).to(torch.bfloat16).to(dev)
+    vn = torch.randn((2, 37, 2, 128), generator=g).to(torch.bfloat16).to(dev)
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    pools1 = [x[k].to(dev) for k in ("k_cache", "v_cache", "k_side")]
+    pools2 = [t.clone() for t in pools1]
+    da.append(kn, vn, x["block_table"].to(dev), pos, *pools1, rope_theta=5e5, pos_host=lens)
+    call = da.prepare_append(kn, vn, x["block_table"].to(dev), pos, *pools2, rope_theta=5e5, pos_host=lens)
+    call()
+    torch.cuda.synchronize()
+    for a, b in zip(pools1, pools2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

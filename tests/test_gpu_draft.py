@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
     dict(mode="full", kappa=0.2, n0=256),
     dict(mode="fold", window=300, alpha=4.0, beta=0.5, kappa=0.1, n0=64, rope="none"),
 ], ids=["full", "window", "fold", "full-kappa", "fold-kappa-nope"])
-@pytest.mark.parametrize("d,T,G", [(128, 4, 4), (64, 8, 2), (128, 1, 8)])
+@pytest.mark.parametrize("d,T,G", [(128, 4, 4), (64, 8, 2), (128, 1, 8), (128, 32, 1)])
 def test_decode_then_merge_draft(kw, d, T, G):
     import draft_attention_amd as da
     dev = torch.device("cuda:0")
@@ -45,3 +45,25 @@ def test_decode_then_merge_draft(kw, d, T, G):
     print(f"merge_draft {kw} d={d} T={T} G={G}: max|dout|={dout:.3e} max|dlse|={dlse:.3e}", flush=True)
     assert np.all(np.isfinite(out.cpu().numpy()))
     assert dout <= 1e-2 and dlse <= 1e-3
+
+
+def test_prepared_merge_draft_matches_the_direct_call():
+    import draft_attention_amd as da
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(63)
+    B, T, Hq, Hkv, d = 3, 6, 8, 2, 128
+    q = torch.randn((B, T, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    kd = torch.randn((B, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vd = torch.randn((B, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    out0 = torch.randn((B, T, Hq, d), generator=g, device=dev)
+    lse0 = torch.randn((B, T, Hq), generator=g, device=dev)
+    lens = [100, 2000, 7]
+    ctx = torch.tensor(lens, dtype=torch.int32, device=dev)
+    kw = dict(num_blocks=200, max_blocks_per_seq=130, num_kv_heads=Hkv, ctx_lens=lens, kappa=0.1, n0=64)
+    o1, l1 = out0.clone(), lse0.clone()
+    da.merge_draft(q, kd, vd, ctx, o1, l1, **kw)
+    o2, l2 = out0.clone(), lse0.clone()
+    call = da.prepare_merge_draft(q, kd, vd, ctx, o2, l2, **kw)
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
