@@ -31,6 +31,12 @@
 // four waves' states merge through LDS into one record per item and row.
 // Pass 2 merges the per-item (max, sums, unnormalised output) records with the
 // log-sum-exp rule, then combines FOLD's local and far partitions with beta.
+// On the single-launch path there is no pass 2: each workgroup marks its item
+// done, and a workgroup that finds every item of its (sequence, kv head) done
+// performs that merge itself (records and flags travel through device-scope
+// accesses, since the eight XCDs' L2 caches are not coherent with each other).
+// Small batches receive their lengths and item offsets with the launch
+// arguments, so neither kernel starts with a dependent read of ctx_len.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
