@@ -11,10 +11,12 @@ Modules
                         written separately from ``reference`` so that each one
                         pins the other on tiny cases.
 
-Pins (``tests/test_oracle_pins.py``, ``tests/golden/``): hand-derived closed
-forms, brute force on tiny inputs, and the reductions the pages fix
-(window >= context is full attention; FOLD with alpha=1, beta=0 is one softmax
-over the union; kappa=0 is the unmodified drafter; weights sum to 1).
+Pins (``tests/test_oracle_pins.py``): hand-derived closed forms, brute force on
+tiny inputs, and the reductions the pages fix (window >= context is full
+attention; FOLD with alpha=1, beta=0 is one softmax over the union; kappa=0 is
+the unmodified drafter; weights sum to 1). The pages print no worked numeric
+example of the attention, so ``tests/golden/closed_forms.json`` holds cases
+worked out by hand from their definitions, each with its derivation.
 
 Parity unpinned: the functional forms of FOLD's alpha/beta combination and of
 SharpDraft's s(n). The pages print no formula for either; this library fixes

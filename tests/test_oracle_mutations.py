@@ -68,6 +68,7 @@ def test_unmodified_copy_passes(tmp_path):
     copy.write_text(open(SRC).read())
     env = dict(os.environ, ORACLE_REFERENCE_PATH=str(copy))
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                          os.path.join(ROOT, "tests", "test_golden.py")],
                          capture_output=True, text=True, env=env, cwd=ROOT, timeout=600)
     assert res.returncode == 0, res.stdout[-2000:]
