@@ -234,10 +234,6 @@ __device__ __forceinline__ void seq_prefix_table(int32_t b, const SeqTable& t, i
 // time. Each wave keeps its own online-softmax state; at the end the states
 // are merged through LDS and the workgroup writes one record per query row.
 constexpr int kWaves = 4;
-#ifndef DA_PREFETCH_STEPS
-#define DA_PREFETCH_STEPS 1
-#endif
-
 
 template <int D>
 struct StepRegs {
@@ -277,7 +273,6 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   const bool vhi = (g >> 1) != 0;    // value keys 8g..8g+7 live in the second block for g >= 2
   const bool sharp = FAR && (a.alpha != 1.f);
   const float alpha = a.alpha;
-  constexpr int PF = DA_PREFETCH_STEPS;
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -401,27 +396,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   };
 
   int32_t s = wave;
-  if (s >= nsteps) {
-  } else if constexpr (PF == 2) {
-    // Loads run two of this wave's steps ahead of the compute (three buffers).
-    StepRegs<D> ra, rb, rc;
-    issue(s, ra);
-    if (s + kWaves < nsteps) issue(s + kWaves, rb);
-    for (;;) {
-      if (s + 2 * kWaves < nsteps) issue(s + 2 * kWaves, rc);
-      compute(s, ra);
-      s += kWaves;
-      if (s >= nsteps) break;
-      if (s + 2 * kWaves < nsteps) issue(s + 2 * kWaves, ra);
-      compute(s, rb);
-      s += kWaves;
-      if (s >= nsteps) break;
-      if (s + 2 * kWaves < nsteps) issue(s + 2 * kWaves, rb);
-      compute(s, rc);
-      s += kWaves;
-      if (s >= nsteps) break;
-    }
-  } else {
+  if (s < nsteps) {
     // Loads run one of this wave's steps ahead of the compute (two buffers).
     StepRegs<D> ra, rb;
     issue(s, ra);
