@@ -72,11 +72,21 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(read=None) -> str:
+    """sha256 of the streaming kernel's sources with // comments and blank lines
+    removed, so that a comment edit does not retire the recorded counters."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                text = f.read().decode()
+        else:
+            text = read(rel)
+        for line in text.splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 
