@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--launch", default="auto", choices=["auto", "two_pass", "single"])
     ap.add_argument("--window", type=int, default=None, help="override the run's window (window / fold modes)")
+    ap.add_argument("--contiguous-blocks", action="store_true",
+                    help="allocate each sequence's blocks in order instead of the shuffled block table")
     ap.add_argument("--op", default="decode", choices=["decode", "append", "merge_draft"],
                     help="decode (the hot path, default) or one of the NEXT-row kernels")
     ap.add_argument("--case", default=None, help="append: decode | prefill; merge_draft: 1m | batch16")
@@ -133,7 +135,7 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes": n, "launches": 3}), flush=True)
 
 
-def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False, launch="auto"):
+def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False, launch="auto", shuffle=True):
     """Generate inputs on the GPU, time `steps` decode calls; returns a result dict."""
     import torch
 
@@ -142,7 +144,7 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
 
     dev = torch.device("cuda:0")
     x = synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed, device=dev,
-                          fold=kw["mode"] == "fold", needle_frac=w.needle_frac, fill="zero")
+                          fold=kw["mode"] == "fold", needle_frac=w.needle_frac, fill="zero", shuffle=shuffle)
     side = x["k_side"] if kw["mode"] == "fold" else None
     out = torch.empty((len(w.ctx_lens), w.T, w.Hq, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((len(w.ctx_lens), w.T, w.Hq), dtype=torch.float32, device=dev)
@@ -466,7 +468,7 @@ def main():
     if args.window is not None:
         kw["window"] = args.window
     r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys, graph=args.graph,
-                      launch=args.launch)
+                      launch=args.launch, shuffle=not args.contiguous_blocks)
     gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
     p1 = r["bytes"] / (r["pass1_ms"] * 1e-3) / 1e9
     tag = f"{w.name}/{kw['mode']}"
@@ -507,6 +509,7 @@ def main():
                    "ctx_len": w.ctx_lens[0] if len(w.ctx_lens) == 1 else w.ctx_lens,
                    "draft_tokens": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "block_size": 16,
                    "split_keys": r["chunk"], "launch": r["launch"],
+                   "block_table": "in order" if args.contiguous_blocks else "shuffled",
                    "alpha": kw.get("alpha", 1.0), "beta": kw.get("beta", 0.0),
                    "kappa": kw.get("kappa", 0.0)},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
