@@ -145,7 +145,8 @@ def test_query_scaling_batched_ragged(launch):
 
 
 @pytest.mark.parametrize("split,launch", [(32, "two_pass"), (64, "two_pass"), (96, "two_pass"), (512, "two_pass"),
-                                          (4096, "two_pass"), (160, "single"), (512, "single"), (4096, "single")])
+                                          (4096, "two_pass"), (65536, "two_pass"), (160, "single"), (512, "single"),
+                                          (4096, "single"), (65536, "single")])
 def test_split_size_sweep(split, launch):
     x = synth.make_inputs(ctx_lens=[9000, 333], T=4, Hq=8, Hkv=2, d=128, seed=12, fold=True)
     for kw in (dict(mode="full"), dict(mode="window", window=1000, n_sink=4),
