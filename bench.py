@@ -447,8 +447,8 @@ def bench_merge_draft(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path shards by sequence, kv head or key range, but no multi-GPU path is built).",
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported. The path shards by sequence, "
+              "kv head or key range, but no multi-GPU path is implemented.",
               file=sys.stderr)
         sys.exit(2)
     if args.calib_copy:

@@ -166,7 +166,7 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
     keyheads += (int64_t)n * Hkv;
   }
 
-  // Kernel coverage of this build.
+  // Kernel coverage of the library.
   if (p->head_dim != 64 && p->head_dim != 128) return DRAFT_ATTN_ENOTSUP;
   const int32_t G = Hq / Hkv;
   const int64_t R = (int64_t)G * T;
@@ -338,7 +338,7 @@ const char* draft_attn_strerror(int status) {
     case DRAFT_ATTN_EINVAL: return "invalid argument";
     case DRAFT_ATTN_ENOSPC: return "workspace too small";
     case DRAFT_ATTN_EHIP: return "HIP launch error";
-    case DRAFT_ATTN_ENOTSUP: return "shape not supported by this build";
+    case DRAFT_ATTN_ENOTSUP: return "shape not supported by the library's kernels";
     default: return "unknown status";
   }
 }

@@ -145,9 +145,9 @@ extern "C" {
 #define DRAFT_ATTN_EINVAL (-1)   /* bad argument, shape, pointer or alignment */
 #define DRAFT_ATTN_ENOSPC (-2)   /* workspace_bytes below draft_attn_workspace_size() */
 #define DRAFT_ATTN_EHIP (-3)     /* the HIP runtime reported a launch error */
-#define DRAFT_ATTN_ENOTSUP (-4)  /* valid, but this build has no kernel for it */
+#define DRAFT_ATTN_ENOTSUP (-4)  /* valid, but the library has no kernel for it */
 
-/* Kernel support of this build: head_dim 64 or 128, block_size 16, and
+/* Kernel support of the library: head_dim 64 or 128, block_size 16, and
  * G * T <= DRAFT_ATTN_MAX_ROWS query rows per (sequence, kv head). */
 #define DRAFT_ATTN_MAX_ROWS 32
 
