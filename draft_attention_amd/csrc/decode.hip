@@ -1064,6 +1064,7 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
       mis(out, 8) || mis(lse, 4) || mis(block_table, 4) || mis(ctx_len_dev, 4) || mis(workspace, 256))
     return DRAFT_ATTN_EINVAL;
   if (workspace_bytes < pr.workspace_bytes) return DRAFT_ATTN_ENOSPC;
+  log_plan(p, pr);
 
   const int D = p->head_dim;
   char* ws = (char*)workspace;

@@ -3,6 +3,8 @@
 #include "host.h"
 
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "plan.h"
@@ -215,6 +217,22 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   out->workspace_bytes = align_up(out->acc_offset + nrows * (size_t)p->head_dim * sizeof(float), 256);
   if (out->workspace_bytes == 0) out->workspace_bytes = 256;
   return DRAFT_ATTN_OK;
+}
+
+void log_plan(const draft_attn_params* p, const Prepared& pr) {
+  static const bool enabled = [] {
+    const char* v = getenv("DRAFT_ATTN_LOG");
+    return v != nullptr && v[0] == '1';
+  }();
+  if (!enabled) return;
+  static const char* const kModes[] = {"full", "window", "fold"};
+  fprintf(stderr,
+          "draft_attn_decode: B=%d T=%d Hq=%d Hkv=%d d=%d mode=%s W=%d sinks=%d alpha=%g beta=%g kappa=%g "
+          "chunk=%d items=%lld max_items_per_group=%d rows=%d launch=%s out=%s\n",
+          p->num_seqs, p->num_draft_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, kModes[p->mode], p->window,
+          p->n_sink, (double)p->alpha, (double)p->beta, (double)p->kappa, pr.chunk, (long long)pr.total_items,
+          pr.max_group_items, pr.rows, pr.single ? "single" : "two_pass",
+          p->out_dtype == DRAFT_ATTN_OUT_BF16 ? "bf16" : "f32");
 }
 
 int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host) {

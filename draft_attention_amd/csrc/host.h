@@ -31,4 +31,8 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
 // Checks the scalar arguments and host positions of draft_attn_append.
 int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host);
 
+// With DRAFT_ATTN_LOG=1 in the environment (read once), prints a decode call's
+// plan to stderr: shapes, mode, chunk size, work items and launch shape.
+void log_plan(const draft_attn_params* p, const Prepared& pr);
+
 }  // namespace da

@@ -102,6 +102,10 @@
  * Errors: every check runs on the host before anything is enqueued, and a
  * non-zero return means nothing was enqueued. DRAFT_ATTN_EHIP reports a launch
  * failure seen by hipGetLastError() after enqueueing.
+ *
+ * Debugging: with DRAFT_ATTN_LOG=1 in the environment (read once, at the first
+ * call), draft_attn_decode prints each call's plan to stderr: shapes, mode,
+ * chunk size, work items and launch shape. Nothing else reads the environment.
  */
 #ifndef DRAFT_ATTN_H
 #define DRAFT_ATTN_H

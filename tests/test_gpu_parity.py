@@ -435,3 +435,22 @@ def test_single_and_two_pass_agree_on_the_benchmark_shapes():
         dlse = float((l1 - l2).abs().max())
         print(f"single vs two-pass {kw}: max|dout|={dout:.2e} max|dlse|={dlse:.2e}", flush=True)
         assert dout <= 1e-4 and dlse <= 1e-5
+
+
+def test_plan_log_on_request(tmp_path):
+    # DRAFT_ATTN_LOG=1 is read once per process, so the call runs in a short child process.
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import torch, draft_attention_amd as da, synth\n"
+            "x = synth.make_inputs(ctx_lens=[3000, 40], T=2, Hq=8, Hkv=2, d=128, seed=1, device='cuda')\n"
+            "da.decode(x['q'], x['k_cache'], x['v_cache'], x['block_table'], x['ctx_len'], ctx_lens=[3000, 40],\n"
+            "          mode='window', window=512, n_sink=4)\n"
+            "torch.cuda.synchronize()\n")
+    env = dict(os.environ, DRAFT_ATTN_LOG="1")
+    res = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True, timeout=180)
+    assert res.returncode == 0, res.stderr[-2000:]
+    line = [ln for ln in res.stderr.splitlines() if ln.startswith("draft_attn_decode:")]
+    assert len(line) == 1 and "B=2 T=2 Hq=8 Hkv=2 d=128 mode=window W=512 sinks=4" in line[0], res.stderr[-2000:]
+    assert "launch=" in line[0] and "items=" in line[0]
