@@ -81,10 +81,12 @@
  *                not read and may hold anything (e.g. -1); an entry that is read
  *                and lies outside [0, num_blocks) is treated as a block of
  *                masked keys (never dereferenced).
- *   ctx_len_dev  int32 [B] on the device, read by the kernels;
- *   ctx_len_host int32 [B] on the host, the same values, read for validation,
- *                grid and workspace sizing. A mismatch gives wrong results but
- *                no out-of-bounds access.
+ *   ctx_len_dev  int32 [B] on the device, the same values as ctx_len_host;
+ *                the kernels read it when B > 32 (smaller batches receive the
+ *                host values with the launch arguments);
+ *   ctx_len_host int32 [B] on the host, read for validation, grid and
+ *                workspace sizing. A mismatch gives wrong results but no
+ *                out-of-bounds access.
  *   out          [B][T][Hq][d], written: fp32 (8-byte aligned) or, with
  *                out_dtype DRAFT_ATTN_OUT_BF16, bf16 rounded to nearest even
  *                from the fp32 result (8-byte aligned).
