@@ -195,6 +195,30 @@ def _host_i32(values):
     return arr
 
 
+def _expect(t, name, dtype, shape, device):
+    """Argument check of the binding: the C ABI sees only pointers, so shapes, dtypes,
+    device and contiguity are checked here. shape entries of None match any size."""
+    if device.type != "cuda":
+        raise ValueError(f"{name}: tensors must be on a GPU (cuda) device, got {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() != len(shape) or any(want is not None and got != want for got, want in zip(t.shape, shape)):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple('*' if x is None else x for x in shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _check_cache(k_cache, v_cache, k_side, Hkv, d, device):
+    import torch
+    NB = k_cache.shape[0]
+    _expect(k_cache, "k_cache", torch.bfloat16, (NB, Hkv, d // 8, 16, 8), device)
+    _expect(v_cache, "v_cache", torch.bfloat16, (NB, Hkv, d, 16), device)
+    if k_side is not None:
+        _expect(k_side, "k_side", torch.bfloat16, (NB, Hkv, d // 8, 16, 8), device)
+
+
 def workspace_size(params: Params, ctx_lens) -> int:
     n = ctypes.c_size_t(0)
     st = lib.draft_attn_workspace_size(ctypes.byref(params), _host_i32(ctx_lens), ctypes.byref(n))
@@ -259,10 +283,18 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
 
     B, T, Hq, d = q.shape
     Hkv = k_cache.shape[1]
+    dev = q.device
+    _expect(q, "q", torch.bfloat16, (B, T, Hq, d), dev)
+    _check_cache(k_cache, v_cache, k_side, Hkv, d, dev)
+    _expect(block_table, "block_table", torch.int32, (B, None), dev)
+    _expect(ctx_len, "ctx_len", torch.int32, (B,), dev)
     if ctx_lens is None:
         ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
+    if len(ctx_lens) != B:
+        raise ValueError(f"ctx_lens: {len(ctx_lens)} lengths for {B} sequences")
     visit_ptr, visit_stride = 0, 0
     if debug_visit is not None:
+        _expect(debug_visit, "debug_visit", torch.uint8, (B, None), dev)
         visit_ptr, visit_stride = debug_visit.data_ptr(), debug_visit.shape[1]
     p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
                     num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
@@ -270,11 +302,12 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
                     softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                     split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
                     fold_variant=fold_variant, launch=launch, out_dtype=out_dtype)
-    dev = q.device
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=_out_torch_dtype(p.out_dtype), device=dev)
+    _expect(out, "out", _out_torch_dtype(p.out_dtype), (B, T, Hq, d), dev)
     if lse is None:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    _expect(lse, "lse", torch.float32, (B, T, Hq), dev)
     need = workspace_size(p, ctx_lens)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -299,38 +332,35 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
     out / lse / workspace are allocated with torch when not given. launch: "auto",
     "two_pass" or "single"; out_dtype: "f32" or "bf16" (the dtype of out).
     """
-    import torch
+    call = prepare(q, k_cache, v_cache, block_table, ctx_len, mode=mode, window=window, n_sink=n_sink, alpha=alpha,
+                   beta=beta, kappa=kappa, n0=n0, softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
+                   k_side=k_side, ctx_lens=ctx_lens, out=out, lse=lse, workspace=workspace, stream=stream,
+                   split_keys=split_keys, debug_visit=debug_visit, fold_variant=fold_variant, launch=launch,
+                   out_dtype=out_dtype)
+    return call(prof_events=prof_events)
 
+
+def _check_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side):
+    import torch
+    B, n_new, Hkv, d = k_new.shape
+    dev = k_new.device
+    _expect(k_new, "k_new", torch.bfloat16, (B, n_new, Hkv, d), dev)
+    _expect(v_new, "v_new", torch.bfloat16, (B, n_new, Hkv, d), dev)
+    _expect(block_table, "block_table", torch.int32, (B, None), dev)
+    _expect(pos, "pos", torch.int32, (B,), dev)
+    _check_cache(k_cache, v_cache, k_side, Hkv, d, dev)
+
+
+def _check_merge(q, k_draft, v_draft, ctx_len, out, lse, num_kv_heads):
+    import torch
     B, T, Hq, d = q.shape
-    Hkv = k_cache.shape[1]
-    if ctx_lens is None:
-        ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
-    visit_ptr, visit_stride = 0, 0
-    if debug_visit is not None:
-        visit_ptr, visit_stride = debug_visit.data_ptr(), debug_visit.shape[1]
-    p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
-                    num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
-                    window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
-                    softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
-                    split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
-                    prof_events=prof_events, fold_variant=fold_variant, launch=launch,
-                    out_dtype=out_dtype)
     dev = q.device
-    if out is None:
-        out = torch.empty((B, T, Hq, d), dtype=_out_torch_dtype(p.out_dtype), device=dev)
-    if lse is None:
-        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
-    need = workspace_size(p, ctx_lens)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
-    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    st = lib.draft_attn_decode(ctypes.byref(p), ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side),
-                               ptr(block_table), ptr(ctx_len), _host_i32(ctx_lens), ptr(out), ptr(lse),
-                               ptr(workspace), workspace.numel() * workspace.element_size(), s)
-    if st != OK:
-        raise DraftAttnError(st, "draft_attn_decode")
-    return out, lse
+    _expect(q, "q", torch.bfloat16, (B, T, Hq, d), dev)
+    _expect(k_draft, "k_draft", torch.bfloat16, (B, T, num_kv_heads, d), dev)
+    _expect(v_draft, "v_draft", torch.bfloat16, (B, T, num_kv_heads, d), dev)
+    _expect(ctx_len, "ctx_len", torch.int32, (B,), dev)
+    _expect(out, "out", torch.float32, (B, T, Hq, d), dev)
+    _expect(lse, "lse", torch.float32, (B, T, Hq), dev)
 
 
 def make_append_params(*, num_seqs, num_new, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
@@ -351,6 +381,7 @@ def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, *, rop
     import torch
 
     B, n_new, Hkv, d = k_new.shape
+    _check_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side)
     if pos_host is None:
         pos_host = [int(x) for x in pos.cpu().tolist()]
     p = make_append_params(num_seqs=B, num_new=n_new, num_kv_heads=Hkv, head_dim=d, num_blocks=k_cache.shape[0],
@@ -384,6 +415,7 @@ def prepare_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None
     import torch
 
     B, n_new, Hkv, d = k_new.shape
+    _check_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side)
     if pos_host is None:
         pos_host = [int(x) for x in pos.cpu().tolist()]
     p = make_append_params(num_seqs=B, num_new=n_new, num_kv_heads=Hkv, head_dim=d, num_blocks=k_cache.shape[0],
@@ -403,6 +435,7 @@ def prepare_merge_draft(q, k_draft, v_draft, ctx_len, out, lse, *, num_blocks, m
     import torch
 
     B, T, Hq, d = q.shape
+    _check_merge(q, k_draft, v_draft, ctx_len, out, lse, num_kv_heads)
     if ctx_lens is None:
         ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
     p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=num_kv_heads, head_dim=d,
@@ -425,6 +458,7 @@ def merge_draft(q, k_draft, v_draft, ctx_len, out, lse, *, num_blocks, max_block
     import torch
 
     B, T, Hq, d = q.shape
+    _check_merge(q, k_draft, v_draft, ctx_len, out, lse, num_kv_heads)
     if ctx_lens is None:
         ctx_lens = [int(x) for x in ctx_len.cpu().tolist()]
     p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=num_kv_heads, head_dim=d,

@@ -395,3 +395,41 @@ def test_merge_draft_refuses_bf16_output():
     st = da().lib.draft_attn_merge_draft(ctypes.byref(p), 0x10000, 0x20000, 0x30000, 0x60000, host, 0x70000,
                                          0x80000, None)
     assert st == -4
+
+
+# ----------------------------------------------------------------------------- binding argument checks
+def test_binding_rejects_host_tensors_and_wrong_dtypes():
+    # These checks run before any GPU call, so they are safe without a GPU.
+    import torch
+    q = torch.zeros((1, 2, 4, 64), dtype=torch.bfloat16)
+    k = torch.zeros((3, 1, 8, 16, 8), dtype=torch.bfloat16)
+    v = torch.zeros((3, 1, 64, 16), dtype=torch.bfloat16)
+    table = torch.zeros((1, 3), dtype=torch.int32)
+    ctx = torch.tensor([40], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        da().decode(q, k, v, table, ctx, ctx_lens=[40])
+    with pytest.raises(ValueError, match="GPU"):
+        da().append(q[:, :, :1], q[:, :, :1], table, ctx, k, v, pos_host=[0])
+    with pytest.raises(ValueError, match="GPU"):
+        da().merge_draft(q, q[:, :, :1], q[:, :, :1], ctx, torch.zeros((1, 2, 4, 64)), torch.zeros((1, 2, 4)),
+                         num_blocks=3, max_blocks_per_seq=3, num_kv_heads=1, ctx_lens=[40])
+
+
+def test_binding_expect_checks_dtype_shape_and_contiguity():
+    import torch
+    dev = torch.device("cuda", 0)            # only compared, never used to allocate
+    t = torch.zeros((2, 3), dtype=torch.float32)
+
+    class Fake:                               # a CPU tensor that reports a GPU device
+        def __init__(self, x):
+            self._x = x
+        def __getattr__(self, k):
+            return getattr(self._x, k)
+        device = dev
+    da()._expect(Fake(t), "x", torch.float32, (2, None), dev)
+    with pytest.raises(ValueError, match="dtype"):
+        da()._expect(Fake(t.to(torch.float64)), "x", torch.float32, (2, 3), dev)
+    with pytest.raises(ValueError, match="shape"):
+        da()._expect(Fake(t), "x", torch.float32, (3, 3), dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        da()._expect(Fake(t.t()), "x", torch.float32, (3, 2), dev)
