@@ -19,7 +19,8 @@ FULL, WINDOW, FOLD = 0, 1, 2
 ROPE_NEOX, ROPE_NONE = 0, 1
 OK, EINVAL, ENOSPC, EHIP, ENOTSUP = 0, -1, -2, -3, -4
 MAX_ROWS = 32
-ABI_VERSION = 2
+ABI_VERSION = 3
+PLAN_ITEM_INTS = 7
 _MODES = {"full": FULL, "window": WINDOW, "fold": FOLD}
 _ROPES = {"neox": ROPE_NEOX, "none": ROPE_NONE}
 FOLD_B, FOLD_JOINT, FOLD_VIRTUAL = 0, 1, 2
@@ -228,19 +229,21 @@ def workspace_size(params: Params, ctx_lens) -> int:
 
 
 def plan(params: Params, ctx_lens):
-    """Work items {seq, kv_head, key_begin, key_end, partition} and the chunk size."""
+    """Work items {seq, kv_head, range_begin, range_end, partition, first_step,
+    step_stride} (the item reads the range's 32-key steps first_step,
+    first_step + step_stride, ...) and the chunk size."""
     host = _host_i32(ctx_lens)
     total = ctypes.c_int64(0)
     chunk = ctypes.c_int32(0)
     st = lib.draft_attn_plan(ctypes.byref(params), host, None, 0, ctypes.byref(total), ctypes.byref(chunk), None)
     if st != OK:
         raise DraftAttnError(st, "draft_attn_plan")
-    buf = (ctypes.c_int32 * (5 * max(total.value, 1)))()
+    buf = (ctypes.c_int32 * (PLAN_ITEM_INTS * max(total.value, 1)))()
     st = lib.draft_attn_plan(ctypes.byref(params), host, buf, total.value, ctypes.byref(total),
                              ctypes.byref(chunk), None)
     if st != OK:
         raise DraftAttnError(st, "draft_attn_plan")
-    items = [tuple(buf[5 * i:5 * i + 5]) for i in range(total.value)]
+    items = [tuple(buf[PLAN_ITEM_INTS * i:PLAN_ITEM_INTS * (i + 1)]) for i in range(total.value)]
     return items, int(chunk.value)
 
 

@@ -12,11 +12,12 @@
 // The exact definitions this code computes are stated in include/draft_attn.h.
 //
 // Design. The call is bound by HBM: every visible key costs 4*d bytes of K and V
-// read once. Pass 1 splits the key axis of every (sequence, kv head) into work
-// items of C keys (plan.h). A 256-thread workgroup streams one item; its four
-// waves take interleaved steps of two 16-token blocks (32 keys) and each keeps
-// the whole GQA group x draft-token row set (R <= 32 rows) of its kv head in
-// registers, so each K/V byte is loaded exactly once:
+// read once. Pass 1 deals the 32-key steps (two 16-token blocks) of every
+// (sequence, kv head) round-robin to work items of at most C keys (plan.h). A
+// 256-thread workgroup streams one item; its four waves take interleaved steps
+// of the item and each keeps the whole GQA group x draft-token row set
+// (R <= 32 rows) of its kv head in registers, so each K/V byte is loaded
+// exactly once:
 //   S^T[key][row] = K . Q^T   on v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q rows)
 //   online softmax per row    in the MFMA output layout: lane (row = l%16) holds
 //                             keys 4*(l/16)+r, so row statistics reduce with two
@@ -228,10 +229,10 @@ __device__ __forceinline__ void seq_prefix_table(int32_t b, const SeqTable& t, i
 }
 
 // ---------------------------------------------------------------- pass 1
-// A work item (a chunk of C keys of one sequence, kv head and partition) is
-// streamed by a workgroup of kWaves waves; wave w takes the chunk's steps
-// w, w + kWaves, ..., so the four waves read neighbouring blocks at the same
-// time. Each wave keeps its own online-softmax state; at the end the states
+// A work item (at most C keys of one sequence, kv head and range: the range's
+// steps first, first + stride, ...) is streamed by a workgroup of kWaves
+// waves; wave w takes the item's steps w, w + kWaves, ... Each wave keeps its
+// own online-softmax state; at the end the states
 // are merged through LDS and the workgroup writes one record per query row.
 constexpr int kWaves = 4;
 
@@ -252,16 +253,16 @@ struct WaveState {
 
 template <int D, int RT, bool FAR, bool LO>
 __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* sbid, int32_t b, int32_t kvh,
-                                             int32_t kb, int32_t ke, int32_t part, float c2,
+                                             const Item& it, float c2,
                                              const bf16x8 (&qh)[RT][D / 32], const bf16x8 (&ql)[RT][D / 32],
                                              WaveState<D, RT>& st) {
   constexpr int KS = D / 32, NT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, i16 = lane & 15, g = lane >> 4;
   const __bf16* __restrict__ kpool = FAR ? a.ks : a.k;
   const __bf16* __restrict__ vpool = a.v;
-  const int32_t blk0 = kb >> 4;
-  const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
-  const int32_t nsteps = (nblk + 1) >> 1;
+  const int32_t nsteps = it.steps;
+  const int32_t ka = it.a, ke = it.e;
+  const int32_t vmark = it.part + 1;
   // Key tile t of a step is block t of the step; MFMA row i reads slot
   // pi(i) = (i & 3) + 4*((i >> 3) & 1) + 8*((i >> 2) & 1). In the key layout
   // [c8][slot][8] one load instruction (fixed k-step) then covers channel groups
@@ -307,16 +308,16 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   };
 
   auto compute = [&](int32_t s, StepRegs<D>& r) {
-    const int32_t key0 = (blk0 + 2 * s) * 16;
-    const bool clean = key0 >= kb && key0 + 32 <= ke && r.id0 >= 0 && r.id1 >= 0;
-    // key (relative to key0) is scored iff its block is valid and it lies in [kb, ke)
+    const int32_t key0 = item_step_key(it, s);
+    const bool clean = key0 >= ka && key0 + 32 <= ke && r.id0 >= 0 && r.id1 >= 0;
+    // key (relative to key0) is scored iff its block is valid and it lies in the range
     auto key_ok = [&](int32_t rel) {
       const int32_t id = rel >= 16 ? r.id1 : r.id0;
       const int32_t key = key0 + rel;
-      return id >= 0 && key >= kb && key < ke;
+      return id >= 0 && key >= ka && key < ke;
     };
     if (a.visit != nullptr && lane < 32 && key_ok(lane))
-      a.visit[(int64_t)b * a.visit_stride + key0 + lane] = (uint8_t)(part + 1);
+      a.visit[(int64_t)b * a.visit_stride + key0 + lane] = (uint8_t)vmark;
     if (!clean) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -652,8 +653,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
   const int32_t rel = w - si.base;
   const int32_t kvh = rel / si.n, kidx = rel - kvh * si.n;
   const Ranges rg = seq_ranges(L, a.mode, a.W, a.S);
-  int32_t kb, ke, part;
-  item_bounds(rg, kidx, a.C, &kb, &ke, &part);
+  const Item it = item_of(rg, kidx, a.C);
 
   // Logit scale in the log2 domain: softmax_scale * s(n) * log2(e).
   const int32_t n = visible_count(L, a.mode, a.W, a.S);
@@ -681,14 +681,16 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
     }
   }
 
-  // Block ids of the chunk, validated, plus one pad entry for the last step's pair.
-  const int32_t blk0 = kb >> 4;
-  const int32_t nblk = ((ke - 1) >> 4) - blk0 + 1;
+  // Block ids of the item's steps (two per step), validated; the second block
+  // of a range's last step may lie past the range and reads as absent.
+  const int32_t nblk = 2 * it.steps;
+  const int32_t last_blk = (it.e - 1) >> 4;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  for (int32_t j = tid; j < nblk + 1; j += 256) {
+  for (int32_t j = tid; j < nblk; j += 256) {
+    const int32_t blk = (item_step_key(it, j >> 1) >> 4) + (j & 1);
     int32_t id = -1;
-    if (j < nblk && blk0 + j < a.max_blocks) {
-      id = trow[blk0 + j];
+    if (blk <= last_blk && blk < a.max_blocks) {
+      id = trow[blk];
       if (id < 0 || id >= a.num_blocks) id = -1;
     }
     sbid[j] = id;
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
   __syncthreads();
 
   WaveState<D, RT> st;
-  const bool far_part = FOLDK && part == kPartFar;
+  const bool far_part = FOLDK && it.part == kPartFar;
   if (far_part) {
     if (a.rope == DRAFT_ATTN_ROPE_NEOX) {
       // Far query q_far = R(-P_v) q, P_v = L - W - 1 [FOLD]. Lane (i16, g) holds
@@ -729,12 +731,12 @@ __global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
             ql[rt][ks + KS / 2][e] = (__bf16)(y2 - (float)h2);
           }
         }
-      stream_steps<D, RT, true, true>(a, sbid, b, kvh, kb, ke, part, c2, qh, ql, st);
+      stream_steps<D, RT, true, true>(a, sbid, b, kvh, it, c2, qh, ql, st);
     } else {
-      stream_steps<D, RT, true, false>(a, sbid, b, kvh, kb, ke, part, c2, qh, ql, st);
+      stream_steps<D, RT, true, false>(a, sbid, b, kvh, it, c2, qh, ql, st);
     }
   } else {
-    stream_steps<D, RT, false, false>(a, sbid, b, kvh, kb, ke, part, c2, qh, ql, st);
+    stream_steps<D, RT, false, false>(a, sbid, b, kvh, it, c2, qh, ql, st);
   }
 
   // ---- merge the waves: common row maxima, rescale, sum through two LDS slots.

@@ -304,10 +304,9 @@ int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int
     for (int32_t h = 0; h < p->num_kv_heads; ++h) {
       for (int32_t k = 0; k < n; ++k, ++w) {
         if (items && w < capacity) {
-          int32_t kb, ke, part;
-          da::item_bounds(r, k, pr.chunk, &kb, &ke, &part);
-          int32_t* it = items + 5 * w;
-          it[0] = b; it[1] = h; it[2] = kb; it[3] = ke; it[4] = part;
+          const da::Item t = da::item_of(r, k, pr.chunk);
+          int32_t* it = items + DRAFT_ATTN_PLAN_ITEM_INTS * w;
+          it[0] = b; it[1] = h; it[2] = t.a; it[3] = t.e; it[4] = t.part; it[5] = t.first; it[6] = t.stride;
         }
       }
     }

@@ -4,14 +4,20 @@
 // "Windowed-MTP: Removing the Full-Context Draft-KV Tax at Million-Token
 // Context", Abstract, and the local/far split of "FOLD: Position-Free Far
 // Memory with Local Order for Long-Context Speculative Decoding", summary).
-// Given a target chunk size P (a multiple of 32 keys), a range of len keys is
-// cut into ceil(len / P) near-equal chunks of round_up_32(ceil(len / np)) keys,
-// counted from the range's first key, so a chunk never straddles a range or
-// partition boundary and no chunk exceeds P keys. Work items are ordered
-// sequence-major, then kv head, then range, then chunk; the ranges of
-// partition 0 (keys from k_cache) come before partition 1 (FOLD far keys from
-// k_side). The kernels recompute this decomposition from ctx_len on the device
-// instead of reading a work list, so nothing is copied from the host per call.
+// A range [a, e) is read in steps of 32 keys: pairs of 16-token blocks counted
+// from the range's first block, a / 16 (keys of a step outside [a, e) are
+// masked). Given a target P (a multiple of 32 keys), the range's steps are
+// dealt round-robin to np = ceil(steps / (P / 32)) work items: item k takes
+// steps k, k + np, k + 2 np, ... So no item reads more than P keys, the items
+// of a range differ by at most one step, every block of a range belongs to one
+// item, and the items of a range read neighbouring steps at the same time
+// rather than places P keys apart (which, with blocks allocated in order,
+// would send every workgroup to addresses a large power of two apart). Work
+// items are ordered sequence-major, then kv head, then range, then item; the
+// ranges of partition 0 (keys from k_cache) come before partition 1 (FOLD far
+// keys from k_side). The kernels recompute this decomposition from ctx_len on
+// the device instead of reading a work list, so nothing is copied from the host
+// per call.
 #pragma once
 
 #include <stdint.h>
@@ -63,19 +69,15 @@ DA_HD Ranges seq_ranges(int32_t L, int32_t mode, int32_t W, int32_t S) {
   return make_ranges(1, 0, ws, kPartFar, 0, 0, kPartMain);
 }
 
-// Chunk length for a range of len > 0 keys under target P: np = ceil(len / P)
-// near-equal chunks, rounded up to whole 32-key steps (never above P).
-DA_HD int32_t range_chunk_len(int32_t len, int32_t P) {
-  const int32_t np = (len + P - 1) / P;
-  const int32_t c = (len + np - 1) / np;
-  return (c + 31) & ~31;
+// Steps of the range [a, e): ceil(blocks / 2) over its blocks a / 16 .. (e - 1) / 16.
+DA_HD int32_t range_steps(int32_t a, int32_t e) {
+  return e > a ? ((((e - 1) >> 4) - (a >> 4)) >> 1) + 1 : 0;
 }
 
-// Number of chunks covering [a, e).
+// Number of work items of the range [a, e) under target P.
 DA_HD int32_t range_chunks(int32_t a, int32_t e, int32_t P) {
-  if (e <= a) return 0;
-  const int32_t len = e - a, c = range_chunk_len(len, P);
-  return (len + c - 1) / c;
+  const int32_t per = P >> 5;  // steps per item at most
+  return (range_steps(a, e) + per - 1) / per;
 }
 
 // Work items of one (sequence, kv head); *n_main receives those of partition 0.
@@ -98,18 +100,32 @@ DA_HD int32_t visible_count(int32_t L, int32_t mode, int32_t W, int32_t S) {
   return L;
 }
 
-// Bounds of item k (0 <= k < seq_items) of a (sequence, kv head).
-DA_HD void item_bounds(const Ranges& r, int32_t k, int32_t P, int32_t* kb, int32_t* ke,
-                       int32_t* part) {
+// Work item k (0 <= k < seq_items) of a (sequence, kv head): its range, its
+// partition and its steps first, first + stride, ... (steps in all).
+struct Item {
+  int32_t a, e;    // the range [a, e)
+  int32_t part;
+  int32_t first;   // first step, counted within the range
+  int32_t stride;  // the range's item count
+  int32_t steps;   // steps of this item (>= 1)
+};
+
+DA_HD Item item_of(const Ranges& r, int32_t k, int32_t P) {
   const int32_t c0 = r.n > 0 ? range_chunks(r.a0, r.e0, P) : 0;
-  const bool first = k < c0;
-  const int32_t a = first ? r.a0 : r.a1;
-  const int32_t e = first ? r.e0 : r.e1;
-  const int32_t kk = first ? k : k - c0;
-  const int32_t c = range_chunk_len(e - a, P);
-  *kb = a + kk * c;
-  *ke = imin(e, *kb + c);
-  *part = first ? r.p0 : r.p1;
+  const bool in0 = k < c0;
+  Item it;
+  it.a = in0 ? r.a0 : r.a1;
+  it.e = in0 ? r.e0 : r.e1;
+  it.part = in0 ? r.p0 : r.p1;
+  it.first = in0 ? k : k - c0;
+  it.stride = in0 ? c0 : range_chunks(r.a1, r.e1, P);
+  it.steps = it.stride > 0 ? (range_steps(it.a, it.e) - it.first + it.stride - 1) / it.stride : 0;
+  return it;
+}
+
+// First key of step s (0 <= s < it.steps) of an item; the step covers 32 keys.
+DA_HD int32_t item_step_key(const Item& it, int32_t s) {
+  return ((it.a >> 4) + 2 * (it.first + s * it.stride)) << 4;
 }
 
 }  // namespace da

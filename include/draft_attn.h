@@ -119,7 +119,7 @@
 extern "C" {
 #endif
 
-#define DRAFT_ATTN_ABI_VERSION 2
+#define DRAFT_ATTN_ABI_VERSION 3
 
 /* modes */
 #define DRAFT_ATTN_FULL 0
@@ -184,8 +184,8 @@ typedef struct draft_attn_params {
   int64_t debug_visit_stride;  /* >= max L when debug_visit is set */
   void* prof_events[2];        /* optional hipEvent_t pair recorded on `stream` just
                                   before and just after the streaming pass; NULL: off */
-  int32_t split_keys;          /* keys per work item: 0 = chosen by the library, else a
-                                  multiple of 32 in [32, 65536] */
+  int32_t split_keys;          /* most keys per work item: 0 = chosen by the library,
+                                  else a multiple of 32 in [32, 65536] */
   int32_t fold_variant;        /* DRAFT_ATTN_FOLD_B (default), _JOINT or _VIRTUAL */
   int32_t launch;              /* DRAFT_ATTN_LAUNCH_AUTO (default), _TWO_PASS or _SINGLE.
                                   SINGLE needs at most DRAFT_ATTN_MAX_GROUP_ITEMS work
@@ -197,6 +197,9 @@ typedef struct draft_attn_params {
                                   written by the merge kernel) */
   int32_t out_dtype;           /* DRAFT_ATTN_OUT_F32 (default) or _BF16 */
 } draft_attn_params;
+
+/* int32 values per work item written by draft_attn_plan. */
+#define DRAFT_ATTN_PLAN_ITEM_INTS 7
 
 /* Work items one workgroup merges on the single-launch path. */
 #define DRAFT_ATTN_MAX_GROUP_ITEMS 64
@@ -224,11 +227,19 @@ int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_c
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only introspection of the work decomposition a call would use: the
- * chunk size in keys (*chunk_keys), the launch shape (*launch: _TWO_PASS or
- * _SINGLE) and the work items in launch order, each {seq, kv_head, key_begin,
- * key_end, partition} with partition 0 for keys read from k_cache and 1 for
- * FOLD far keys read from k_side. Writes at most `capacity` items to `items`
- * (may be NULL) and the total to *n_items; chunk_keys and launch may be NULL. */
+ * chunk size in keys (*chunk_keys: the most keys of one work item), the launch
+ * shape (*launch: _TWO_PASS or _SINGLE) and the work items in launch order,
+ * DRAFT_ATTN_PLAN_ITEM_INTS int32 each:
+ *   {seq, kv_head, range_begin, range_end, partition, first_step, step_stride}.
+ * A work item reads part of one key range [range_begin, range_end) of a
+ * sequence's visible set (partition 0: keys read from k_cache; 1: FOLD far keys
+ * read from k_side). The range is read in steps of 32 keys, pairs of 16-token
+ * blocks counted from block range_begin / 16; the item takes the range's steps
+ * first_step, first_step + step_stride, ... (step_stride is the range's item
+ * count), keeping the keys of each step that lie in the range. The items of a
+ * range thus share its steps round-robin and cover it exactly once. Writes at
+ * most `capacity` items to `items` (may be NULL) and the total to *n_items;
+ * chunk_keys and launch may be NULL. */
 int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t* items,
                     int64_t capacity, int64_t* n_items, int32_t* chunk_keys, int32_t* launch);
 

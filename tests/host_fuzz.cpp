@@ -54,7 +54,7 @@ int main() {
     if (st != DRAFT_ATTN_OK) continue;
     ++accepted;
     if (n > 200000) continue;
-    std::vector<int32_t> items(5 * (size_t)(n > 0 ? n : 1));
+    std::vector<int32_t> items(DRAFT_ATTN_PLAN_ITEM_INTS * (size_t)(n > 0 ? n : 1));
     int64_t n2 = 0;
     if (draft_attn_plan(&p, lens.data(), items.data(), n, &n2, &chunk, nullptr) != DRAFT_ATTN_OK || n2 != n) return 1;
     if (launch != DRAFT_ATTN_LAUNCH_SINGLE && launch != DRAFT_ATTN_LAUNCH_TWO_PASS) {
@@ -68,9 +68,9 @@ int main() {
     // Single launch: every (sequence, kv head) has 1..DRAFT_ATTN_MAX_GROUP_ITEMS items.
     std::vector<int64_t> per_group((size_t)p.num_seqs * p.num_kv_heads, 0);
     for (int64_t i = 0; i < n; ++i) {
-      const int32_t* it = &items[5 * i];
+      const int32_t* it = &items[DRAFT_ATTN_PLAN_ITEM_INTS * i];
       const int32_t L = lens[it[0]];
-      if (it[2] < 0 || it[3] > L || it[2] >= it[3] || it[1] >= p.num_kv_heads) {
+      if (it[2] < 0 || it[3] > L || it[2] >= it[3] || it[1] >= p.num_kv_heads || it[5] < 0 || it[5] >= it[6]) {
         printf("item out of range\n");
         return 1;
       }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(da().LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da().lib.draft_attn_version() == 2
+    assert da().lib.draft_attn_version() == 3
 
 
 def test_params_layout_matches_the_c_compiler(tmp_path):
@@ -208,29 +208,46 @@ def test_workspace_independent_of_alpha_beta_kappa():
 
 
 # ----------------------------------------------------------------------------- work decomposition
+def _item_keys(item):
+    """Keys a work item scores, from the documented item format: the 32-key steps
+    first, first + stride, ... of its range, counted from block range_begin // 16,
+    each clipped to [range_begin, range_end)."""
+    _, _, a, e, _, first, stride = item
+    base = a // 16
+    nsteps = ((e - 1) // 16 - base) // 2 + 1
+    parts = [np.arange(max(a, 16 * (base + 2 * t)), min(e, 16 * (base + 2 * t) + 32))
+             for t in range(first, nsteps, stride)]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
 def _check_plan(mode, W, S, lens, Hkv, split):
     p = params(num_seqs=len(lens), num_kv_heads=Hkv, num_q_heads=Hkv * 2, num_draft_tokens=2, mode=mode,
                window=W, n_sink=S, split_keys=split, max_blocks_per_seq=max(1, (max(lens) + 15) // 16),
                num_blocks=1 << 20)
     items, C = da().plan(p, lens)
     assert C % 32 == 0 and (split == 0 or C == split)
-    seen = {}
+    seen, ranges = {}, {}
     prev = (-1, -1, -1)
-    for (b, h, kb, ke, part) in items:
-        assert 0 <= b < len(lens) and 0 <= h < Hkv and kb < ke and part in (0, 1)
-        assert ke - kb <= C, "chunk longer than the target"
+    for item in items:
+        b, h, a, e, part, first, stride = item
+        assert 0 <= b < len(lens) and 0 <= h < Hkv and 0 <= a < e <= lens[b] and part in (0, 1)
+        assert 0 <= first < stride
+        keys = _item_keys(item)
+        assert 0 < keys.size <= C, "item empty or longer than the target"
         assert (b, h, part) >= prev, "launch order is sequence, kv head, partition"
         prev = (b, h, part)
-        seen.setdefault((b, h, part), []).append((kb, ke))
+        seen.setdefault((b, h, part), []).append(keys)
+        ranges.setdefault((b, h, a, e), []).append((first, stride))
+    for (b, h, a, e), fs in ranges.items():
+        stride = fs[0][1]
+        assert fs == [(k, stride) for k in range(stride)], "a range's items take its steps round-robin, in order"
     for b, L in enumerate(lens):
         main, far = oracle.index_sets(L, mode, W, S)
         for h in range(Hkv):
             for part, want in ((0, main), (1, far)):
-                got = np.concatenate([np.arange(kb, ke) for kb, ke in seen.get((b, h, part), [])] or
-                                     [np.zeros(0, dtype=np.int64)])
+                got = np.concatenate(seen.get((b, h, part), []) or [np.zeros(0, dtype=np.int64)])
                 assert np.array_equal(np.sort(got), want), (b, h, part)
-                assert np.unique(got).size == got.size, "overlapping chunks"
-    n = ctypes.c_size_t(0)
+                assert np.unique(got).size == got.size, "overlapping items"
     assert da().workspace_size(p, lens) >= len(items) * 16 * (128 + 4) * 4
 
 
@@ -246,36 +263,42 @@ def test_plan_covers_the_oracle_index_sets():
 
 
 def test_auto_chunk_size_balances_the_workloads():
-    # One sequence of 2^20 keys, 8 kv heads: 256 equal chunks (one per compute unit).
+    # One sequence of 2^20 keys, 8 kv heads: 256 equal items (one per compute unit).
     p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=8, mode="full",
                max_blocks_per_seq=1 << 16, num_blocks=1 << 17)
     items, C = da().plan(p, [1 << 20])
-    assert C == 32768 and len(items) == 256 and {ke - kb for (_, _, kb, ke, _) in items} == {32768}
-    # FOLD at 256K with a 4096 window: the far range splits evenly; no item exceeds C.
+    assert C == 32768 and len(items) == 256 and {_item_keys(it).size for it in items} == {32768}
+    assert {it[6] for it in items} == {32}, "each head's 1024 steps dealt to 32 items"
+    # FOLD at 256K with a 4096 window: no item exceeds C, at most one per compute unit.
     p = params(num_seqs=1, num_q_heads=32, num_kv_heads=8, num_draft_tokens=6, mode="fold", n_sink=0, window=4096,
                max_blocks_per_seq=1 << 14, num_blocks=1 << 15)
     items, C = da().plan(p, [262144])
-    assert len(items) <= 256 and max(ke - kb for (_, _, kb, ke, _) in items) <= C
-    # Ragged batches: every chunk of a range but the last has one length; the last is no longer.
+    assert len(items) <= 256 and max(_item_keys(it).size for it in items) <= C
+    # Ragged batches: the items of a sequence differ by at most one step (plus a
+    # partial last block) and none exceeds C.
     lens = [40000, 300000, 123457]
     p = params(num_seqs=3, num_q_heads=16, num_kv_heads=4, num_draft_tokens=2, mode="full",
                max_blocks_per_seq=(300000 + 15) // 16, num_blocks=1 << 20)
     items, C = da().plan(p, lens)
     for b in range(3):
-        sizes = [ke - kb for (bb, h, kb, ke, _) in items if bb == b and h == 0]
-        assert sum(sizes) == lens[b] and len(set(sizes[:-1])) <= 1 and sizes[-1] <= sizes[0] <= C
+        sizes = [_item_keys(it).size for it in items if it[0] == b and it[1] == 0]
+        assert sum(sizes) == lens[b] and max(sizes) - min(sizes) < 64 and max(sizes) <= C
 
 
-def test_chunk_lengths_are_balanced_and_step_aligned():
+def test_items_deal_a_range_s_steps_round_robin():
     for L in (1, 31, 32, 33, 1000, 4097, 100003):
         for P in (32, 64, 96, 4096):
             p = params(num_seqs=1, mode="full", split_keys=P, max_blocks_per_seq=(L + 15) // 16, num_blocks=1 << 16)
             items, C = da().plan(p, [L])
-            spans = [(kb, ke) for (_, h, kb, ke, _) in items if h == 0]
-            assert spans[0][0] == 0 and spans[-1][1] == L
-            assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
-            assert all((ke - kb) % 32 == 0 for kb, ke in spans[:-1])
-            assert len(spans) == -(-L // P)
+            head0 = [it for it in items if it[1] == 0]
+            nsteps = -(-L // 32)
+            want = -(-nsteps // (P // 32))
+            assert len(head0) == want
+            assert [it[2:] for it in head0] == [(0, L, 0, k, want) for k in range(want)]
+            steps = [len(range(k, nsteps, want)) for k in range(want)]
+            assert max(steps) - min(steps) <= 1 and max(steps) <= P // 32
+            got = np.concatenate([_item_keys(it) for it in head0])
+            assert np.array_equal(np.sort(got), np.arange(L))
 
 
 def test_host_logic_under_sanitizers(tmp_path):
@@ -330,7 +353,7 @@ def test_launch_and_out_dtype_validated():
 
 def _group_counts(items):
     counts = {}
-    for (b, h, _, _, _) in items:
+    for (b, h, *_) in items:
         counts[(b, h)] = counts.get((b, h), 0) + 1
     return counts
 
