@@ -192,19 +192,43 @@ def test_unread_blocks_may_be_invalid():
     assert np.array_equal(out, base)
 
 
-def test_block_shuffle_gives_identical_results():
-    x = synth.make_inputs(ctx_lens=[3000, 50], T=4, Hq=8, Hkv=2, d=128, seed=15, fold=True)
-    NB = x["k_cache"].shape[0]
-    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(1))
+def _relabel_blocks(x, perm):
+    """The same cache with physical block perm[i] moved to position i."""
     inv = torch.argsort(perm)
     t = x["block_table"]
     t2 = torch.where(t >= 0, inv[t.clamp(min=0).long()].to(torch.int32), t)
-    y = dict(x, k_cache=x["k_cache"][perm], v_cache=x["v_cache"][perm], k_side=x["k_side"][perm],
-             block_table=t2)
+    return dict(x, k_cache=x["k_cache"][perm], v_cache=x["v_cache"][perm], k_side=x["k_side"][perm],
+                block_table=t2)
+
+
+def test_block_shuffle_gives_identical_results():
+    x = synth.make_inputs(ctx_lens=[3000, 50], T=4, Hq=8, Hkv=2, d=128, seed=15, fold=True)
+    NB = x["k_cache"].shape[0]
+    y = _relabel_blocks(x, torch.randperm(NB, generator=torch.Generator().manual_seed(1)))
     for kw in (dict(mode="full"), dict(mode="fold", window=512, alpha=2.0, beta=-1.0)):
         a, la = check(x, kw)
         b, lb = check(y, kw)
         assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_in_order_block_table_gives_identical_results():
+    # Blocks allocated in table order (sequence by sequence) against a shuffled
+    # pool, with a split that gives each range many work items, so that the
+    # round-robin dealing of steps crosses many block boundaries.
+    x = synth.make_inputs(ctx_lens=[20000, 1500, 77], T=4, Hq=8, Hkv=2, d=128, seed=16, fold=True)
+    NB = x["k_cache"].shape[0]
+    used = [int(i) for i in x["block_table"].flatten().tolist() if i >= 0]
+    assert len(set(used)) == len(used)
+    rest = sorted(set(range(NB)) - set(used))
+    y = _relabel_blocks(x, torch.tensor(used + rest))
+    t = y["block_table"]
+    assert all(int(t[0, j]) == j for j in range((20000 + 15) // 16)), "table not in order"
+    for split in (0, 1024):
+        for kw in (dict(mode="full"), dict(mode="window", window=3000, n_sink=20),
+                   dict(mode="fold", window=1000, alpha=4.0, beta=-1.0)):
+            a, la = check(x, kw, split=split, label=f"shuffled {kw} split={split}")
+            b, lb = check(y, kw, split=split, label=f"in order {kw} split={split}")
+            assert np.array_equal(a, b) and np.array_equal(la, lb), f"{kw} split={split}"
 
 
 def test_deterministic_and_stream_safe():
