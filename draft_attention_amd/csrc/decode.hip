@@ -419,7 +419,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   }
 }
 
-// Dynamic LDS of pass 1: block ids of the chunk, then the merge buffers.
+// Dynamic LDS of pass 1: block ids of the item, then the merge buffers.
 __host__ __device__ inline size_t pass1_sbid_bytes(int32_t C) { return ((size_t)(C / 16 + 2) * 4 + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t pass1_lds_bytes(int32_t C, int32_t rows_pad, int32_t D) {
   return pass1_sbid_bytes(C) + (size_t)kWaves * rows_pad * (sizeof(float) + sizeof(float2)) +

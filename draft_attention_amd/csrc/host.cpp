@@ -16,7 +16,7 @@ namespace {
 // Chunk-size model. Each work item is streamed by one 4-wave workgroup; the
 // number resident per compute unit is register-limited (compiler resource
 // usage for gfx950: head_dim 128 -> 1; head_dim 64 -> 3 with one row tile, 2
-// with two). With near-equal chunks of at most P keys, r rounds over the
+// with two). With items of at most P keys (near-equal within a range), r rounds over the
 // resident slots take about r * (P + kItemOverheadKeys) key-steps, the
 // overhead being an item's start-up (block-table and query loads before the
 // first K/V load). The planner tries 1..kMaxRounds rounds and keeps the
