@@ -16,15 +16,19 @@ namespace {
 // Chunk-size model. Each work item is streamed by one 4-wave workgroup; the
 // number resident per compute unit is register-limited (compiler resource
 // usage for gfx950: head_dim 128 -> 1; head_dim 64 -> 3 with one row tile, 2
-// with two). With items of at most P keys (near-equal within a range), r rounds over the
-// resident slots take about r * (P + kItemOverheadKeys) key-steps, the
-// overhead being an item's start-up (block-table and query loads before the
-// first K/V load). The planner tries 1..kMaxRounds rounds and keeps the
+// with two). An item's four waves take its 32-key steps in turn, so an item
+// of at most P keys lasts about ceil(P / 128) steps of its busiest wave: P is
+// rounded up to a multiple of 128 keys, which never adds a step to any wave
+// and leaves fewer items (fewer records to merge). With such items, r rounds
+// over the resident slots take about r * (P + kItemOverheadKeys) key-steps,
+// the overhead being an item's start-up (block-table and query loads before
+// the first K/V load). The planner tries 1..kMaxRounds rounds and keeps the
 // cheapest.
 constexpr int32_t kComputeUnits = 256;  // MI355X
 constexpr int64_t kItemOverheadKeys = 256;
 constexpr int32_t kMaxRounds = 4;
 constexpr int32_t kMinAutoChunk = 128;  // one 32-key step per wave
+constexpr int32_t kWaveRoundKeys = 128;  // one 32-key step for each of the four waves
 constexpr int32_t kMaxChunk = 65536;    // bounds the block-id table kept in LDS
 constexpr int32_t kMaxLen = 1 << 30;
 
@@ -62,7 +66,9 @@ int32_t choose_chunk(const draft_attn_params* p, const int32_t* lens, int64_t ke
     const int64_t budget = r * slots;
     int64_t lo = (keyheads + budget - 1) / budget;
     lo = lo < kMinAutoChunk ? kMinAutoChunk : (lo > kMaxChunk ? kMaxChunk : lo);
-    const int32_t P = fit_chunk(p, lens, round_up_32(lo), budget);
+    int32_t P = fit_chunk(p, lens, round_up_32(lo), budget);
+    P = (int32_t)((P + kWaveRoundKeys - 1) / kWaveRoundKeys * kWaveRoundKeys);
+    P = P > kMaxChunk ? kMaxChunk : P;
     const int64_t items = count_items(p, lens, P);
     const int64_t rounds = (items + slots - 1) / slots;
     const int64_t cost = (rounds > 0 ? rounds : 1) * ((int64_t)P + kItemOverheadKeys);
