@@ -226,6 +226,7 @@ def _check_plan(mode, W, S, lens, Hkv, split):
                num_blocks=1 << 20)
     items, C = da().plan(p, lens)
     assert C % 32 == 0 and (split == 0 or C == split)
+    assert split != 0 or C % 128 == 0, "the library's chunk is whole rounds of the four waves' steps"
     seen, ranges = {}, {}
     prev = (-1, -1, -1)
     for item in items:
