@@ -399,17 +399,43 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   int32_t s = wave;
   if (s < nsteps) {
     // Loads run one of this wave's steps ahead of the compute (two buffers).
+    // In the loop every compute starts with the other buffer's loads issued
+    // after its own on every path, so the compiler's wait before it covers
+    // only this step's loads. (With the next issue under a condition inside
+    // the loop, the wait had to cover the newest load as well, which left
+    // almost no loads in flight during the wait.) The last one or two steps
+    // run after the loop.
     StepRegs<D> ra, rb;
     issue(s, ra);
-    for (;;) {
-      if (s + kWaves < nsteps) issue(s + kWaves, rb);
-      compute(s, ra);
-      s += kWaves;
-      if (s >= nsteps) break;
-      if (s + kWaves < nsteps) issue(s + kWaves, ra);
-      compute(s, rb);
-      s += kWaves;
-      if (s >= nsteps) break;
+    if constexpr (!LO) {
+      while (s + 2 * kWaves < nsteps) {
+        issue(s + kWaves, rb);
+        compute(s, ra);
+        issue(s + 2 * kWaves, ra);
+        compute(s + kWaves, rb);
+        s += 2 * kWaves;
+      }
+      if (s + kWaves < nsteps) {
+        issue(s + kWaves, rb);
+        compute(s, ra);
+        compute(s + kWaves, rb);
+      } else {
+        compute(s, ra);
+      }
+    } else {
+      // The rotated far query's lo half takes 32 more registers at two row
+      // tiles; the loop above then spills, so this path keeps one compute
+      // per buffer and the stricter wait (measured faster here).
+      for (;;) {
+        if (s + kWaves < nsteps) issue(s + kWaves, rb);
+        compute(s, ra);
+        s += kWaves;
+        if (s >= nsteps) break;
+        if (s + kWaves < nsteps) issue(s + kWaves, ra);
+        compute(s, rb);
+        s += kWaves;
+        if (s >= nsteps) break;
+      }
     }
   }
 #pragma unroll
