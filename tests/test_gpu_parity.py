@@ -154,6 +154,18 @@ def test_split_size_sweep(split, launch):
         check(x, kw, split=split, label=f"split={split} {launch} {kw}", launch=launch)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_steps_per_wave_count(d):
+    # The streaming loop has a main part (three or more steps left per wave) and
+    # a tail of one or two steps; chunks of 128 m keys give each of the four
+    # waves exactly m steps (the last, ragged item fewer), for m = 1 .. 7.
+    for m in range(1, 8):
+        split = 128 * m
+        x = synth.make_inputs(ctx_lens=[3 * split + 77, split - 16], T=4, Hq=8, Hkv=2, d=d, seed=60 + m, fold=True)
+        for kw in (dict(mode="full"), dict(mode="fold", window=split + 40, alpha=2.0, beta=-1.0)):
+            check(x, kw, split=split, label=f"d={d} {m} steps per wave {kw}")
+
+
 def test_needles_full_attention():
     x = synth.make_inputs(ctx_lens=[30000], T=8, Hq=32, Hkv=8, d=128, seed=13, needle_frac=0.01)
     check(x, dict(mode="full"), label="needles full")
