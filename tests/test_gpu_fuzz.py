@@ -5,6 +5,7 @@ empty sequences), chunk size, launch shape and output dtype all vary. Same
 bars as the parity tests; the visited key set must equal the oracle's."""
 
 import math
+import os
 import random
 
 import numpy as np
@@ -16,7 +17,8 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+# 48 by default; a longer sweep: DRAFT_ATTN_FUZZ_CASES=600
+N_CASES = int(os.environ.get("DRAFT_ATTN_FUZZ_CASES", "48"))
 
 
 def draw(rnd):
@@ -36,7 +38,7 @@ def draw(rnd):
                   fold_variant=rnd.choice(["B", "A", "B'"]))
     if rnd.random() < 0.4:
         kw.update(kappa=rnd.choice([-0.05, 0.1, 0.3]), n0=rnd.choice([1, 16, 256]))
-    split = rnd.choice([0, 0, 32, 96, 256, 1024])
+    split = rnd.choice([0, 0, 32, 96, 256, 384, 640, 1024])
     launch = rnd.choice(["auto", "two_pass", "single"])
     out_dtype = rnd.choice(["f32", "f32", "bf16"])
     needle = rnd.choice([0.0, 0.0, 0.02])
