@@ -287,8 +287,10 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   // K/V are read once per call: nontemporal loads keep them from displacing
   // anything in the caches.
   auto issue = [&](int32_t s, StepRegs<D>& r) {
-    r.id0 = sbid[2 * s];
-    r.id1 = sbid[2 * s + 1];
+    // Every lane reads the same two ids; making them wave-uniform lets the
+    // block base addresses and the step's mask test live in scalar registers.
+    r.id0 = __builtin_amdgcn_readfirstlane(sbid[2 * s]);
+    r.id1 = __builtin_amdgcn_readfirstlane(sbid[2 * s + 1]);
     // masked block: read block 0 (in bounds), values discarded
     const int32_t kid0 = r.id0 < 0 ? 0 : r.id0;
     const int32_t kid1 = r.id1 < 0 ? 0 : r.id1;
@@ -347,11 +349,14 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          float xv = sc[t][rt][rr] * c2;
-          if (!clean && !key_ok(16 * t + srel + rr)) xv = -INFINITY;
-          x[4 * t + rr] = xv;
-        }
+        for (int rr = 0; rr < 4; ++rr) x[4 * t + rr] = sc[t][rt][rr] * c2;
+      if (!clean) {  // wave-uniform: only steps at a range edge or with a missing block
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (!key_ok(16 * t + srel + rr)) x[4 * t + rr] = -INFINITY;
+      }
       float mx = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
