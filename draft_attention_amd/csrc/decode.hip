@@ -658,8 +658,13 @@ __device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int3
   }
 }
 
+// Waves per SIMD, i.e. workgroups per CU, that the kernel is compiled for; the
+// host planner's resident_per_cu() uses the same numbers.
+constexpr int pass1_occupancy(int D, int RT) { return D == 64 ? (RT == 1 ? 3 : 2) : 1; }
+
 template <int D, int RT, bool FOLDK, bool SINGLE>
-__global__ __launch_bounds__(256) void pass1_kernel(const Pass1Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(pass1_occupancy(D, RT))))
+void pass1_kernel(const Pass1Args a) {
   constexpr int KS = D / 32, NT = D / 16, OS = D + 4;  // OS: padded LDS row stride (floats)
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i16 = lane & 15, g = lane >> 4;

@@ -14,8 +14,8 @@ namespace da {
 namespace {
 
 // Chunk-size model. Each work item is streamed by one 4-wave workgroup; the
-// number resident per compute unit is register-limited (compiler resource
-// usage for gfx950: head_dim 128 -> 1; head_dim 64 -> 3 with one row tile, 2
+// number resident per compute unit is set by registers, and the kernel asks the
+// compiler for it (head_dim 128 -> 1; head_dim 64 -> 3 with one row tile, 2
 // with two). An item's four waves take its 32-key steps in turn, so an item
 // of at most P keys lasts about ceil(P / 128) steps of its busiest wave: P is
 // rounded up to a multiple of 128 keys, which never adds a step to any wave
@@ -32,6 +32,8 @@ constexpr int32_t kWaveRoundKeys = 128;  // one 32-key step for each of the four
 constexpr int32_t kMaxChunk = 65536;    // bounds the block-id table kept in LDS
 constexpr int32_t kMaxLen = 1 << 30;
 
+// The streaming kernel requests exactly this occupancy from the compiler
+// (amdgpu_waves_per_eu, pass1_occupancy() in decode.hip), so the two agree.
 int32_t resident_per_cu(int32_t D, int32_t row_tiles) { return D == 128 ? 1 : (row_tiles == 1 ? 3 : 2); }
 
 int32_t round_up_32(int64_t x) { return (int32_t)((x + 31) / 32 * 32); }
