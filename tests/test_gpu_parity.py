@@ -166,6 +166,27 @@ def test_every_steps_per_wave_count(d):
             check(x, kw, split=split, label=f"d={d} {m} steps per wave {kw}")
 
 
+def test_fold_far_logit_precision_at_large_logits():
+    # The rotated far query is held as two bf16 terms (about 17 significant
+    # bits), so far logits, and lse through them, err by about 2^-19 of their
+    # magnitude. Needle keys with a large alpha and kappa push |lse| to
+    # hundreds of nats; the error stays within a small multiple of that, and
+    # without the rotation (same data) it is at fp32 level.
+    x = synth.make_inputs(ctx_lens=[1900, 3000], T=6, Hq=8, Hkv=4, d=64, seed=70, fold=True, needle_frac=0.02)
+    n = np_inputs(x)
+    g = to_dev(x)
+    for rope, rel in (("neox", 2.0 ** -17), ("none", 2.0 ** -20)):
+        kw = dict(mode="fold", window=17, alpha=3.0, beta=0.0, kappa=0.3, n0=1, fold_variant="A", rope=rope)
+        out, lse, _ = run_gpu(g, kw, visit=False)
+        ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], n["block_table"], x["ctx_lens"],
+                            k_side=n["k_side"], rope_theta=5e5, **kw)
+        big = float(np.abs(ref["lse"]).max())
+        assert big > 100, "the case is meant to have large logits"
+        err = np.abs(lse - ref["lse"])
+        assert np.all(err <= rel * np.abs(ref["lse"]) + 1e-5), (rope, float(err.max()), big)
+        assert float(np.abs(out - ref["out"]).max()) <= 1e-2
+
+
 def test_needles_full_attention():
     x = synth.make_inputs(ctx_lens=[30000], T=8, Hq=32, Hkv=8, d=128, seed=13, needle_frac=0.01)
     check(x, dict(mode="full"), label="needles full")
