@@ -255,6 +255,7 @@ template <int D, int RT, bool FAR, bool LO>
 __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* sbid, int32_t b, int32_t kvh,
                                              const Item& it, float c2,
                                              const bf16x8 (&qh)[RT][D / 32], const bf16x8 (&ql)[RT][D / 32],
+                                             const bf16x8 (&qm)[RT][D / 32],
                                              WaveState<D, RT>& st) {
   constexpr int KS = D / 32, NT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, i16 = lane & 15, g = lane >> 4;
@@ -339,6 +340,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][ks], qh[rt][ks], c, 0, 0, 0);
+          if (LO) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][ks], qm[rt][ks], c, 0, 0, 0);
           if (LO) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][ks], ql[rt][ks], c, 0, 0, 0);
         }
         sc[t][rt] = c;
@@ -428,9 +430,10 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
         compute(s, ra);
       }
     } else {
-      // The rotated far query's lo half takes 32 more registers at two row
-      // tiles; the loop above then spills, so this path keeps one compute
-      // per buffer and the stricter wait (measured faster here).
+      // The rotated far query's mid and lo terms take 64 more registers at
+      // two row tiles; the loop above then runs short of registers, so this
+      // path keeps one compute per buffer and the stricter wait (measured
+      // faster here).
       for (;;) {
         if (s + kWaves < nsteps) issue(s + kWaves, rb);
         compute(s, ra);
@@ -698,7 +701,7 @@ void pass1_kernel(const Pass1Args a) {
 
   // Query rows of this kv head (loaded before the block table so both loads are
   // in flight together): row = t * G + (h - kvh * G), zero-padded to 16 * RT.
-  bf16x8 qh[RT][KS], ql[RT][KS];
+  bf16x8 qh[RT][KS], ql[RT][KS], qm[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int32_t row = 16 * rt + i16;
@@ -714,6 +717,7 @@ void pass1_kernel(const Pass1Args a) {
       const bf16x8 qv = *(const bf16x8*)(qp + 32 * ks);  // qp is a valid row even when !ok
       qh[rt][ks] = ok ? qv : z;
       ql[rt][ks] = z;
+      qm[rt][ks] = z;
     }
   }
 
@@ -740,8 +744,10 @@ void pass1_kernel(const Pass1Args a) {
       // Far query q_far = R(-P_v) q, P_v = L - W - 1 [FOLD]. Lane (i16, g) holds
       // channels 32ks + 8g + e; the rotation partner d/2 away sits in k-step
       // ks + KS/2 of the same lane. Angles are formed and reduced mod 2*pi in fp64;
-      // the rotated value is split into bf16 hi + lo so the Q.K^T product keeps
-      // ~16 significant bits of q_far.
+      // the fp32 rotated value is split into three bf16 terms (hi, mid, lo) so
+      // the Q.K^T product keeps q_far's 24 significant bits. (Two terms keep
+      // about 17, which at far logits of hundreds of nats moves lse by a few
+      // 1e-4; the third product costs no measurable time here.)
       const double pv = (double)(L - a.W - 1);
 #pragma unroll
       for (int ks = 0; ks < KS / 2; ++ks)
@@ -763,16 +769,19 @@ void pass1_kernel(const Pass1Args a) {
             const __bf16 h1 = (__bf16)y1, h2 = (__bf16)y2;
             qh[rt][ks][e] = h1;
             qh[rt][ks + KS / 2][e] = h2;
-            ql[rt][ks][e] = (__bf16)(y1 - (float)h1);
-            ql[rt][ks + KS / 2][e] = (__bf16)(y2 - (float)h2);
+            const __bf16 m1 = (__bf16)(y1 - (float)h1), m2 = (__bf16)(y2 - (float)h2);
+            qm[rt][ks][e] = m1;
+            qm[rt][ks + KS / 2][e] = m2;
+            ql[rt][ks][e] = (__bf16)(y1 - (float)h1 - (float)m1);
+            ql[rt][ks + KS / 2][e] = (__bf16)(y2 - (float)h2 - (float)m2);
           }
         }
-      stream_steps<D, RT, true, true>(a, sbid, b, kvh, it, c2, qh, ql, st);
+      stream_steps<D, RT, true, true>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
     } else {
-      stream_steps<D, RT, true, false>(a, sbid, b, kvh, it, c2, qh, ql, st);
+      stream_steps<D, RT, true, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
     }
   } else {
-    stream_steps<D, RT, false, false>(a, sbid, b, kvh, it, c2, qh, ql, st);
+    stream_steps<D, RT, false, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
   }
 
   // ---- merge the waves: common row maxima, rescale, sum through two LDS slots.

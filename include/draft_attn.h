@@ -61,10 +61,9 @@
  *    All three are one softmax over Loc U Far at alpha = 1, beta = 0.
  * Numerics: bf16 inputs; logits, sums and outputs accumulate in fp32, and the
  * probabilities that weight the values are rounded to bf16 (relative to the
- * running maximum, so the dominant key's weight is exactly 1). FOLD's rotated far query is kept as two bf16
- * terms (about 17 significant bits), so far logits, and lse through them, err by
- * about 2^-19 of their magnitude; with DRAFT_ATTN_ROPE_NONE and in the other
- * modes they are at fp32 level.
+ * running maximum, so the dominant key's weight is exactly 1). FOLD's rotated
+ * far query is kept as three bf16 terms (all 24 bits of its fp32 value), so
+ * logits and lse are at fp32 level in every mode.
  *
  * ---------------------------------------------------------------------------
  * Layouts. All tensors are device memory owned by the caller; the library
