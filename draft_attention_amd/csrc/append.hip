@@ -5,14 +5,15 @@
 // and names its bookkeeping as part of the cost. For each newly accepted token
 // at position p this kernel writes the key turned to its own position, R(p) k,
 // into k_cache, the unrotated key into k_side, and the value into v_cache, at the
-// slot the block table gives for p. The rotation is done in fp64 (angles formed
-// and reduced by the fp64 sincos, then advanced by fp64 rotation steps across a
-// few consecutive positions) and rounded once to bf16, to nearest with ties to
-// even: the stored key is the bf16 value nearest to an fp64 rotation that is
-// within a few fp64 ulps of the exact one.
+// slot the block table gives for p. The rotation is done in fp64 (the angle of
+// a block's first slot formed and reduced by the fp64 sincos, then advanced by
+// fp64 rotation steps to the block's other slots) and rounded once to bf16, to
+// nearest with ties to even: the stored key is the bf16 value nearest to an
+// fp64 rotation that is within a few fp64 ulps of the exact one.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "host.h"
 
@@ -32,6 +33,8 @@ struct AppendArgs {
   double omega[64];     // rope_theta^(-2i/D)
   double cos_w[64];     // cos(omega_i), sin(omega_i): one position step
   double sin_w[64];
+  double cos_g[64];     // cos(G omega_i), sin(G omega_i): one slot group of
+  double sin_g[64];     // G = 16 * (D/2) / 256 positions
 };
 
 // fp64 -> bf16 bits, round to nearest, ties to even, for finite values in the
@@ -51,10 +54,30 @@ __device__ __forceinline__ unsigned short bf16_bits_rne(double x) {
 // with row-contiguous loads, rotated there, and written back as whole 16-byte
 // runs of each cache layout: 16 slots of one key octet for k_cache and k_side,
 // 8 slots of one channel for v_cache (a partial run at the edges of the append
-// is written per slot). Rotation: thread (pair i, slot group q) forms the angle
-// of its first slot with the fp64 sincos and advances it one position at a time
-// by the rotation (cos w_i, sin w_i), which adds a few fp64 ulps.
-template <int D>
+// is written per slot). Large appends (NT) load and store nontemporally, since
+// each byte is moved once; small ones (a decode step's accepted tokens) use
+// ordinary accesses, which complete sooner and leave the new slots in cache for
+// the next decode. Rotation: the first D/2 threads form the angle of the block's slot 0
+// for their pair with the fp64 sincos (one per pair, not per thread: the fp64
+// unit, not memory, was the limit otherwise), in wave 0, which stages nothing,
+// so the sincos overlaps the other waves' loads. Wave 0 also turns it to the
+// first slot of every slot group by steps of (cos G w_i, sin G w_i) and leaves
+// those angles and the one-position step (cos w_i, sin w_i) in LDS, so that
+// after the barrier the rotation reads nothing from memory; thread (pair i,
+// slot group q) then advances one position at a time. Each step adds a few
+// fp64 ulps.
+template <bool NT, typename T>
+__device__ __forceinline__ T load_nt(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void store_nt(T v, T* p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   constexpr int NO = D / 8;               // channel octets
   constexpr int HALF = D / 2;             // rotation pairs
@@ -63,6 +86,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   __shared__ __align__(16) __bf16 s_k[16][LD];
   __shared__ __align__(16) __bf16 s_v[16][LD];
   __shared__ __align__(16) __bf16 s_r[16][LD];
+  constexpr int NG = 256 / HALF;          // slot groups of the rotation
+  __shared__ double s_c0[NG][HALF], s_s0[NG][HALF];  // angle of each group's first slot
+  __shared__ double s_cw[HALF], s_sw[HALF];          // one position step
   const int tid = threadIdx.x;
   int64_t w = blockIdx.x;
   const int32_t h = (int32_t)(w % a.Hkv);
@@ -80,32 +106,77 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   const int s0 = (int)(lo64 - (int64_t)j * 16), s1 = (int)(hi64 - (int64_t)j * 16);
   const int32_t i0 = (int32_t)(lo64 - p0);  // index of slot s0's token among the new ones
 
-  // Stage the new tokens' keys and values: one 16-byte octet per thread.
-  for (int e = tid; e < 16 * NO; e += 256) {
-    const int s = e / NO, c = e - s * NO;
-    if (s < s0 || s >= s1) continue;
-    const size_t src = (((size_t)b * a.n_new + (i0 + s - s0)) * a.Hkv + h) * D + 8 * c;
-    *(uint4*)&s_k[s][8 * c] = *(const uint4*)(a.k_new + src);
-    *(uint4*)&s_v[s][8 * c] = *(const uint4*)(a.v_new + src);
+  // Wave 0 forms the block's sincos while waves 1-3 stage the new tokens' keys
+  // and values, 16 slots x D/8 octets of 16 bytes (wave 1 takes two octets per
+  // thread when there are 256). Keeping the sincos off the staging waves keeps
+  // its argument load out of their load queue: a wave's wait for one load also
+  // waits for every load issued before it. A lane whose octet is outside the
+  // new slots loads slot s0's octet and drops it, so that every lane of a wave
+  // issues the same loads.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  static_assert(16 * NO <= 192 + 64, "at most two staged octets per thread");
+  const bool rot = a.rope == DRAFT_ATTN_ROPE_NEOX;
+  if (tid < 64) {
+    if (rot && tid < HALF) {
+      const double om = a.omega[tid], cg = a.cos_g[tid], sg = a.sin_g[tid];
+      s_cw[tid] = a.cos_w[tid];
+      s_sw[tid] = a.sin_w[tid];
+      double sn, cs;
+      sincos((double)((int64_t)j * 16) * om, &sn, &cs);
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        s_c0[q][tid] = cs;
+        s_s0[q][tid] = sn;
+        const double c2 = cs * cg - sn * sg;
+        sn = sn * cg + cs * sg;
+        cs = c2;
+      }
+    }
+  } else {
+    const int e1 = tid - 64, e2 = e1 + 192;
+    const bool has1 = e1 < 16 * NO, has2 = e2 < 16 * NO;  // uniform per wave
+    const int s1a = e1 / NO, c1 = e1 - s1a * NO, s2a = e2 / NO, c2 = e2 - s2a * NO;
+    const bool ok1 = s1a >= s0 && s1a < s1, ok2 = s2a >= s0 && s2a < s1;
+    auto src = [&](bool ok, int ss, int sc) {
+      return (((size_t)b * a.n_new + (i0 + (ok ? ss : s0) - s0)) * a.Hkv + h) * D + 8 * (ok ? sc : 0);
+    };
+    if (has1) {
+      const size_t o1 = src(ok1, s1a, c1);
+      const u32x4 k1 = load_nt<NT>((const u32x4*)(a.k_new + o1));
+      const u32x4 v1 = load_nt<NT>((const u32x4*)(a.v_new + o1));
+      u32x4 k2 = {0u, 0u, 0u, 0u}, v2 = {0u, 0u, 0u, 0u};
+      if (has2) {
+        const size_t o2 = src(ok2, s2a, c2);
+        k2 = load_nt<NT>((const u32x4*)(a.k_new + o2));
+        v2 = load_nt<NT>((const u32x4*)(a.v_new + o2));
+      }
+      if (ok1) {
+        *(u32x4*)&s_k[s1a][8 * c1] = k1;
+        *(u32x4*)&s_v[s1a][8 * c1] = v1;
+      }
+      if (has2 && ok2) {
+        *(u32x4*)&s_k[s2a][8 * c2] = k2;
+        *(u32x4*)&s_v[s2a][8 * c2] = v2;
+      }
+    }
   }
   __syncthreads();
 
   // Rotate: thread (i, q) owns pair (i, i + D/2) of slots q*SPT .. q*SPT + SPT - 1.
-  if (a.rope == DRAFT_ATTN_ROPE_NEOX) {
+  if (rot) {
     const int i = tid % HALF, q = tid / HALF;
-    int sa = q * SPT, sb = sa + SPT;
-    sa = sa > s0 ? sa : s0;
-    sb = sb < s1 ? sb : s1;
-    if (sa < sb) {
-      double sn, cs;
-      sincos((double)((int64_t)j * 16 + sa) * a.omega[i], &sn, &cs);
-      const double cw = a.cos_w[i], sw = a.sin_w[i];
+    const int sa = q * SPT, sb = sa + SPT;
+    if (sa < s1 && sb > s0) {
+      double cs = s_c0[q][i], sn = s_s0[q][i];
+      const double cw = s_cw[i], sw = s_sw[i];
       for (int s = sa; s < sb; ++s) {
-        const double x1 = (double)(float)s_k[s][i], x2 = (double)(float)s_k[s][i + HALF];
-        const unsigned short r1 = bf16_bits_rne(x1 * cs - x2 * sn);
-        const unsigned short r2 = bf16_bits_rne(x1 * sn + x2 * cs);
-        s_r[s][i] = __builtin_bit_cast(__bf16, r1);
-        s_r[s][i + HALF] = __builtin_bit_cast(__bf16, r2);
+        if (s >= s0 && s < s1) {
+          const double x1 = (double)(float)s_k[s][i], x2 = (double)(float)s_k[s][i + HALF];
+          const unsigned short r1 = bf16_bits_rne(x1 * cs - x2 * sn);
+          const unsigned short r2 = bf16_bits_rne(x1 * sn + x2 * cs);
+          s_r[s][i] = __builtin_bit_cast(__bf16, r1);
+          s_r[s][i + HALF] = __builtin_bit_cast(__bf16, r2);
+        }
         const double c2 = cs * cw - sn * sw;
         sn = sn * cw + cs * sw;
         cs = c2;
@@ -122,8 +193,8 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const int c = e / 16, s = e - c * 16;
     if (s < s0 || s >= s1) continue;
     const size_t dst = blk + ((size_t)c * 16 + s) * 8;
-    *(uint4*)(a.k + dst) = *(const uint4*)&kr[s][8 * c];
-    if (a.ks != nullptr) *(uint4*)(a.ks + dst) = *(const uint4*)&s_k[s][8 * c];
+    store_nt<NT>(*(const u32x4*)&kr[s][8 * c], (u32x4*)(a.k + dst));
+    if (a.ks != nullptr) store_nt<NT>(*(const u32x4*)&s_k[s][8 * c], (u32x4*)(a.ks + dst));
   }
   // Values: thread (channel ch, half g) writes slots 8g .. 8g+7 of channel ch.
   for (int e = tid; e < 2 * D; e += 256) {
@@ -135,7 +206,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
       bf16x8_t o;
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = s_v[sa + k][ch];
-      *(bf16x8_t*)dst = o;
+      store_nt<NT>(o, (bf16x8_t*)dst);
     } else {
       for (int k = 0; k < 8; ++k)
         if (sa + k >= s0 && sa + k < s1) dst[k] = s_v[sa + k][ch];
@@ -172,17 +243,31 @@ extern "C" int draft_attn_append(const draft_attn_append_params* p, const void* 
   a.num_blocks = p->num_blocks;
   a.rope = p->rope;
   const int D = p->head_dim;
-  for (int i = 0; i < 64; ++i) {
-    a.omega[i] = i < D / 2 && p->rope == DRAFT_ATTN_ROPE_NEOX ? pow(p->rope_theta, -2.0 * (double)i / (double)D) : 0.0;
-    a.cos_w[i] = cos(a.omega[i]);
-    a.sin_w[i] = sin(a.omega[i]);
+  if (p->rope == DRAFT_ATTN_ROPE_NEOX) {
+    static_assert(16 * (64 / 2) / 256 == 64 / 32 && 16 * (128 / 2) / 256 == 128 / 32, "slot group = d/32 positions");
+    const RopeTable& t = rope_table(p->rope_theta, D);
+    memcpy(a.omega, t.omega, sizeof a.omega);
+    memcpy(a.cos_w, t.cos_w, sizeof a.cos_w);
+    memcpy(a.sin_w, t.sin_w, sizeof a.sin_w);
+    memcpy(a.cos_g, t.cos_g, sizeof a.cos_g);
+    memcpy(a.sin_g, t.sin_g, sizeof a.sin_g);
+  } else {
+    for (double* t : {a.omega, a.cos_w, a.sin_w, a.cos_g, a.sin_g}) memset(t, 0, 64 * sizeof(double));  // unread
   }
   a.span = (p->num_new + 15) / 16 + 1;
   const uint32_t grid = (uint32_t)((int64_t)a.B * a.span * a.Hkv);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  if (D == 64) append_kernel<64><<<grid, 256, 0, s>>>(a);
-  else append_kernel<128><<<grid, 256, 0, s>>>(a);
+  // Streaming (nontemporal) accesses once the append moves more than the
+  // infinity cache could usefully keep: 64 MiB of new keys, side keys and values.
+  const bool nt = (double)a.B * a.n_new * a.Hkv * 10.0 * D > 64.0 * 1024 * 1024;
+  if (D == 64) {
+    if (nt) append_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    else append_kernel<64, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (nt) append_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    else append_kernel<128, false><<<grid, 256, 0, s>>>(a);
+  }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
 }

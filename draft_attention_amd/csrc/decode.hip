@@ -1151,11 +1151,14 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a1.alpha = p->alpha;
   a1.kappa = p->kappa;
   a1.scale = p->softmax_scale;
-  // RoPE frequencies, read only by FOLD's far-query rotation (64 pow calls
-  // would otherwise cost about a microsecond of host time per call).
+  // RoPE frequencies, read only by FOLD's far-query rotation.
   const bool far_rope = p->mode == kFold && p->rope == DRAFT_ATTN_ROPE_NEOX;
-  for (int i = 0; i < kMaxHalfDim; ++i)
-    a1.omega[i] = far_rope && i < D / 2 ? pow(p->rope_theta, -2.0 * (double)i / (double)D) : 0.0;
+  if (far_rope) {
+    static_assert(kMaxHalfDim <= 64, "frequency table size");
+    memcpy(a1.omega, rope_table(p->rope_theta, D).omega, sizeof a1.omega);
+  } else {
+    memset(a1.omega, 0, sizeof a1.omega);
+  }
   memset(&a1.seqs, 0, sizeof(a1.seqs));
   if (p->num_seqs <= kArgSeqs) {
     a1.seqs.nseq = p->num_seqs;

@@ -262,6 +262,23 @@ int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host) {
   return DRAFT_ATTN_OK;
 }
 
+const RopeTable& rope_table(double theta, int32_t d) {
+  static thread_local RopeTable t = {0.0, 0, {}, {}, {}, {}, {}};
+  if (t.d != d || memcmp(&t.theta, &theta, sizeof theta) != 0) {
+    const double g = d / 32;
+    for (int i = 0; i < 64; ++i) {
+      t.omega[i] = i < d / 2 ? pow(theta, -2.0 * (double)i / (double)d) : 0.0;
+      t.cos_w[i] = cos(t.omega[i]);
+      t.sin_w[i] = sin(t.omega[i]);
+      t.cos_g[i] = cos(g * t.omega[i]);
+      t.sin_g[i] = sin(g * t.omega[i]);
+    }
+    t.theta = theta;
+    t.d = d;
+  }
+  return t;
+}
+
 }  // namespace da
 
 extern "C" {

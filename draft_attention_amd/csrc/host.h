@@ -31,6 +31,18 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
 // Checks the scalar arguments and host positions of draft_attn_append.
 int prepare_append(const draft_attn_append_params* p, const int32_t* pos_host);
 
+// NeoX RoPE frequencies for head dim d (at most 128): omega_i = theta^(-2i/d),
+// one position step (cos omega_i, sin omega_i) and one slot-group step of
+// g = d/32 positions (cos g omega_i, sin g omega_i), zero past d/2. A pure
+// function of (theta, d), kept in a per-thread memo: the 64 pow and 192 cos/sin
+// calls would otherwise cost a few microseconds of host time per call.
+struct RopeTable {
+  double theta;
+  int32_t d;
+  double omega[64], cos_w[64], sin_w[64], cos_g[64], sin_g[64];
+};
+const RopeTable& rope_table(double theta, int32_t d);
+
 // With DRAFT_ATTN_LOG=1 in the environment (read once), prints a decode call's
 // plan to stderr: shapes, mode, chunk size, work items and launch shape.
 void log_plan(const draft_attn_params* p, const Prepared& pr);

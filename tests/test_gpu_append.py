@@ -149,3 +149,40 @@ def test_prepared_append_matches_the_direct_call():
     torch.cuda.synchronize()
     for a, b in zip(pools1, pools2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_large_append_streaming_path_matches_oracle():
+    # An append that moves more than 64 MiB takes the kernel's streaming
+    # (nontemporal) variant: 30000 tokens x 2 kv heads x 1280 bytes. Every new
+    # slot must be written (and nothing else: the pools start as NaN), and two
+    # samples of 1000 tokens, at the start (mid-block) and at the end of the
+    # append, must equal the oracle's appends bit for bit.
+    da = _da()
+    dev = torch.device("cuda:0")
+    d, Hkv, n_new, start = 128, 2, 30000, 777
+    assert n_new * Hkv * 10 * d > 64 * 1024 * 1024
+    first, last = start // 16, (start + n_new - 1) // 16
+    NB = last - first + 1
+    table = torch.full((1, last + 1), -1, dtype=torch.int32)
+    table[0, first:] = torch.arange(NB, dtype=torch.int32)
+    g = torch.Generator().manual_seed(9)
+    kn = (torch.randn((1, n_new, Hkv, d), generator=g) * 2).to(torch.bfloat16)
+    vn = torch.randn((1, n_new, Hkv, d), generator=g).to(torch.bfloat16)
+    nan_k = torch.full((NB, Hkv, d // 8, 16, 8), float("nan"), dtype=torch.bfloat16)
+    nan_v = torch.full((NB, Hkv, d, 16), float("nan"), dtype=torch.bfloat16)
+    gk, gv, gs = nan_k.to(dev), nan_v.to(dev), nan_k.clone().to(dev)
+    da.append(kn.to(dev), vn.to(dev), table.to(dev), torch.tensor([start], dtype=torch.int32, device=dev),
+              gk, gv, gs, rope="neox", rope_theta=5e5, pos_host=[start])
+    torch.cuda.synchronize()
+    ck, cv, cs = _np(gk), _np(gv), _np(gs)
+    for pool in (ck, cv, cs):
+        assert int((~np.isnan(pool)).sum()) == n_new * Hkv * d
+    tab = table.numpy()
+    for a in (0, n_new - 1000):
+        sel = slice(a, a + 1000)
+        rk, rv, rs = oracle.append(_np(kn)[:, sel], _np(vn)[:, sel], tab, [start + a], _np(nan_k), _np(nan_v),
+                                   _np(nan_k), rope="neox", rope_theta=5e5)
+        for ref, got in ((rk, ck), (rv, cv), (rs, cs)):
+            m = ~np.isnan(ref)
+            assert int(m.sum()) == 1000 * Hkv * d
+            assert np.array_equal(ref[m], got[m])
