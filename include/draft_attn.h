@@ -102,9 +102,11 @@
  *                single-launch path; every call leaves them zero.
  *
  * Calls are asynchronous on `stream` (a hipStream_t). The library allocates
- * nothing, synchronises nothing and keeps no mutable global state: concurrent
- * calls on different streams with distinct workspaces are safe; calls that
- * share a workspace must not overlap in time.
+ * nothing, synchronises nothing and keeps no shared mutable state (its only
+ * cache is a per-thread memo of the RoPE frequency table, a pure function of
+ * rope_theta and head_dim): concurrent calls on different streams with
+ * distinct workspaces are safe; calls that share a workspace must not overlap
+ * in time.
  *
  * Errors: every check runs on the host before anything is enqueued, and a
  * non-zero return means nothing was enqueued. DRAFT_ATTN_EHIP reports a launch
