@@ -722,18 +722,29 @@ void pass1_kernel(const Pass1Args a) {
   }
 
   // Block ids of the item's steps (two per step), validated; the second block
-  // of a range's last step may lie past the range and reads as absent.
+  // of a range's last step may lie past the range and reads as absent. Each
+  // thread issues up to eight table loads before it waits for any (a loop of
+  // load-then-store waits one round trip per id). A slot with no id loads
+  // entry 0 of the row, which exists, and drops it.
   const int32_t nblk = 2 * it.steps;
   const int32_t last_blk = (it.e - 1) >> 4;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  for (int32_t j = tid; j < nblk; j += 256) {
-    const int32_t blk = (item_step_key(it, j >> 1) >> 4) + (j & 1);
-    int32_t id = -1;
-    if (blk <= last_blk && blk < a.max_blocks) {
-      id = trow[blk];
-      if (id < 0 || id >= a.num_blocks) id = -1;
+  constexpr int kStageUnroll = 8;
+  for (int32_t j0 = 0; j0 < nblk; j0 += 256 * kStageUnroll) {
+    int32_t ids[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int32_t j = j0 + 256 * u + tid;
+      const int32_t blk = (item_step_key(it, j >> 1) >> 4) + (j & 1);
+      const bool ok = j < nblk && blk <= last_blk && blk < a.max_blocks;
+      const int32_t id = trow[ok ? blk : 0];
+      ids[u] = ok && id >= 0 && id < a.num_blocks ? id : -1;
     }
-    sbid[j] = id;
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int32_t j = j0 + 256 * u + tid;
+      if (j < nblk) sbid[j] = ids[u];
+    }
   }
   __syncthreads();
 
