@@ -151,15 +151,16 @@ def test_prepared_append_matches_the_direct_call():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_large_append_streaming_path_matches_oracle():
+@pytest.mark.parametrize("d,n_new", [(128, 30000), (64, 60000)])
+def test_large_append_streaming_path_matches_oracle(d, n_new):
     # An append that moves more than 64 MiB takes the kernel's streaming
-    # (nontemporal) variant: 30000 tokens x 2 kv heads x 1280 bytes. Every new
+    # (nontemporal) variant: n_new tokens x 2 kv heads x 10 d bytes. Every new
     # slot must be written (and nothing else: the pools start as NaN), and two
     # samples of 1000 tokens, at the start (mid-block) and at the end of the
     # append, must equal the oracle's appends bit for bit.
     da = _da()
     dev = torch.device("cuda:0")
-    d, Hkv, n_new, start = 128, 2, 30000, 777
+    Hkv, start = 2, 777
     assert n_new * Hkv * 10 * d > 64 * 1024 * 1024
     first, last = start // 16, (start + n_new - 1) // 16
     NB = last - first + 1
