@@ -60,9 +60,9 @@ def parse():
     ap.add_argument("--window", type=int, default=None, help="override the run's window (window / fold modes)")
     ap.add_argument("--contiguous-blocks", action="store_true",
                     help="allocate each sequence's blocks in order instead of the shuffled block table")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "merge_draft"],
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "merge_draft", "decode_draft"],
                     help="decode (the hot path, default) or one of the NEXT-row kernels")
-    ap.add_argument("--case", default=None, help="append: decode | prefill; merge_draft: 1m | batch16")
+    ap.add_argument("--case", default=None, help="append: decode | prefill; merge_draft: 1m | batch16; decode_draft: window_128k | window_1m")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -444,6 +444,52 @@ def bench_merge_draft(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_decode_draft(args):
+    """A draft step's whole attention: the cache part (draft_attn_decode) merged with
+    the draft tokens' causal part, as two calls (decode, then merge_draft: three
+    kernels) against the fused call (draft_attn_decode_draft: two kernels). Cases:
+    'window_128k' (WINDOW 2048 + 4 sinks at 131072 keys, 4 draft tokens) and
+    'window_1m' (WINDOW 4096 + 4 at 2^20 keys, 8 draft tokens); 32/8 heads, d = 128.
+    Reports us per step for both, eager calls."""
+    import torch
+
+    import draft_attention_amd as da
+    import synth
+
+    case = args.case or "window_128k"
+    L, T, W = (131072, 4, 2048) if case == "window_128k" else (1 << 20, 8, 4096)
+    Hq, Hkv, d = 32, 8, 128
+    dev = torch.device("cuda:0")
+    x = synth.make_inputs(ctx_lens=[L], T=T, Hq=Hq, Hkv=Hkv, d=d, seed=args.seed, device=dev, fill="zero")
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    kd = torch.randn((1, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vd = torch.randn((1, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    kw = dict(mode="window", window=W, n_sink=4, ctx_lens=[L])
+    dec = da.prepare(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], **kw)
+    mrg = da.prepare_merge_draft(x["q"], kd, vd, x["ctx_len"], dec.out, dec.lse, num_blocks=x["k_cache"].shape[0],
+                                 max_blocks_per_seq=x["block_table"].shape[1], num_kv_heads=Hkv, mode="window",
+                                 window=W, n_sink=4, ctx_lens=[L])
+    fused = da.prepare(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], k_draft=kd, v_draft=vd,
+                       **kw)
+
+    def two_calls():
+        dec()
+        mrg()
+
+    t2, w2 = _event_mean_us(two_calls, args.steps, args.warmup)
+    t1, w1 = _event_mean_us(fused, args.steps, args.warmup)
+    line = {"metric": "draft step attention with draft tokens: us per step", "value": round(t1, 2), "unit": "us",
+            "op": "decode_draft", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "us_per_step_fused": round(t1, 2), "us_per_step_two_calls": round(t2, 2),
+            "us_per_step_wall_fused": round(w1, 2), "us_per_step_wall_two_calls": round(w2, 2),
+            "config": {"case": case, "ctx_len": L, "draft_tokens": T, "window": W, "n_sink": 4, "q_heads": Hq,
+                       "kv_heads": Hkv, "head_dim": d},
+            "roofline": None, "cpu_baseline": None,
+            "note": "latency-bound steps: the fused call saves the separate merge launch"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -459,6 +505,9 @@ def main():
         return
     if args.op == "merge_draft":
         bench_merge_draft(args)
+        return
+    if args.op == "decode_draft":
+        bench_decode_draft(args)
         return
     import synth
 

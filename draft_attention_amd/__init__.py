@@ -106,6 +106,9 @@ def _load():
     lib.draft_attn_workspace_size.restype = ctypes.c_int
     lib.draft_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, ctypes.c_size_t, vp]
     lib.draft_attn_decode.restype = ctypes.c_int
+    lib.draft_attn_decode_draft.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                            vp]
+    lib.draft_attn_decode_draft.restype = ctypes.c_int
     lib.draft_attn_plan.argtypes = [P, i32p, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), i32p, i32p]
     lib.draft_attn_plan.restype = ctypes.c_int
     lib.draft_attn_merge_draft.argtypes = [P, vp, vp, vp, vp, i32p, vp, vp, vp]
@@ -261,8 +264,9 @@ class PreparedDecode:
     """One decode call with its arguments marshalled once; calling it enqueues the
     call again on the stream given at preparation (or on `stream`)."""
 
-    def __init__(self, params, args, out, lse, keep):
+    def __init__(self, params, args, out, lse, keep, fused=False):
         self.params, self.args, self.out, self.lse, self._keep = params, args, out, lse, keep
+        self._fn = lib.draft_attn_decode_draft if fused else lib.draft_attn_decode
 
     def __call__(self, stream=None, prof_events=None):
         p = self.params
@@ -271,16 +275,17 @@ class PreparedDecode:
         else:
             p.prof_events[0] = p.prof_events[1] = None
         args = self.args if stream is None else self.args[:-1] + (int(stream),)
-        st = lib.draft_attn_decode(ctypes.byref(p), *args)
+        st = self._fn(ctypes.byref(p), *args)
         if st != OK:
-            raise DraftAttnError(st, "draft_attn_decode")
+            raise DraftAttnError(st, self._fn.__name__)
         return self.out, self.lse
 
 
 def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
             beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
             ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
-            debug_visit=None, fold_variant="B", launch="auto", out_dtype="f32") -> PreparedDecode:
+            debug_visit=None, fold_variant="B", launch="auto", out_dtype="f32", k_draft=None,
+            v_draft=None) -> PreparedDecode:
     """Marshal the arguments of decode() once (same meaning as there)."""
     import torch
 
@@ -317,17 +322,30 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     host = _host_i32(ctx_lens)
-    args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side), ptr(block_table), ptr(ctx_len), host, ptr(out),
-            ptr(lse), ptr(workspace), workspace.numel() * workspace.element_size(), s)
-    keep = (q, k_cache, v_cache, k_side, block_table, ctx_len, workspace, debug_visit, host)
-    return PreparedDecode(p, args, out, lse, keep)
+    fused = k_draft is not None or v_draft is not None
+    if fused:
+        _expect(k_draft, "k_draft", torch.bfloat16, (B, T, Hkv, d), dev)
+        _expect(v_draft, "v_draft", torch.bfloat16, (B, T, Hkv, d), dev)
+        args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side), ptr(block_table), ptr(ctx_len), host,
+                ptr(k_draft), ptr(v_draft), ptr(out), ptr(lse), ptr(workspace),
+                workspace.numel() * workspace.element_size(), s)
+    else:
+        args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side), ptr(block_table), ptr(ctx_len), host, ptr(out),
+                ptr(lse), ptr(workspace), workspace.numel() * workspace.element_size(), s)
+    keep = (q, k_cache, v_cache, k_side, block_table, ctx_len, workspace, debug_visit, host, k_draft, v_draft)
+    return PreparedDecode(p, args, out, lse, keep, fused=fused)
 
 
 def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, n_sink=0, alpha=1.0,
            beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
            ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
-           debug_visit=None, prof_events=None, fold_variant="B", launch="auto", out_dtype="f32"):
+           debug_visit=None, prof_events=None, fold_variant="B", launch="auto", out_dtype="f32",
+           k_draft=None, v_draft=None):
     """Enqueue draft_attn_decode on the current (or given) stream; returns (out, lse).
+
+    With k_draft / v_draft (bf16 [B,T,Hkv,d], the step's draft keys and values),
+    enqueues draft_attn_decode_draft instead: the same result merged with each
+    draft token's causal attention over draft keys 0..t.
 
     q bf16 [B,T,Hq,d]; k_cache / k_side bf16 [NB,Hkv,d/8,16,8]; v_cache bf16 [NB,Hkv,d,16];
     block_table int32 [B,MB]; ctx_len int32 [B] on the device; ctx_lens: the same
@@ -339,7 +357,7 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
                    beta=beta, kappa=kappa, n0=n0, softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                    k_side=k_side, ctx_lens=ctx_lens, out=out, lse=lse, workspace=workspace, stream=stream,
                    split_keys=split_keys, debug_visit=debug_visit, fold_variant=fold_variant, launch=launch,
-                   out_dtype=out_dtype)
+                   out_dtype=out_dtype, k_draft=k_draft, v_draft=v_draft)
     return call(prof_events=prof_events)
 
 

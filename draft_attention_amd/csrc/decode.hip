@@ -44,6 +44,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "draft_part.h"
 #include "host.h"
 #include "plan.h"
 
@@ -96,9 +97,12 @@ struct Pass2Args {
   const int32_t* ctx_len;
   void* out;
   float* lse;
+  const __bf16* q;   // draft part (fused call only): query rows [B][T][Hq][D]
+  const __bf16* kd;  // draft keys [B][T][Hkv][D], rotated at the draft positions
+  const __bf16* vd;  // draft values [B][T][Hkv][D]
   int32_t B, T, Hq, Hkv, G, R, rows_pad;
-  int32_t mode, W, S, C, total_items, fold_variant, out_bf16;
-  float alpha, beta;
+  int32_t mode, W, S, C, total_items, fold_variant, out_bf16, n0;
+  float alpha, beta, kappa, scale;
   SeqTable seqs;
 };
 
@@ -898,7 +902,10 @@ void pass1_kernel(const Pass1Args a) {
 // of them. Longer rows stream the records in tiles.
 constexpr int kFastItems = 8;
 
-template <int D>
+// TM > 0: the fused call. Wave 0 also forms the row's draft part (draft keys
+// 0..t of the step, draft_part.h; its loads are issued with the records') and
+// the row is written already merged with it.
+template <int D, int TM>
 __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   constexpr int NQ = D / 4;     // float4 channel quads per row
   constexpr int NG = 256 / NQ;  // item groups
@@ -927,6 +934,15 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   const size_t rp = (size_t)a.rows_pad;
   const int64_t n = i1 - i0;
   const float* accrow = a.acc + row * (size_t)D + 4 * q4;
+  const int32_t t = row / a.G;
+  const int32_t head = kvh * a.G + (row - t * a.G);
+  const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
+  __shared__ float s_od[(TM > 0 ? D : 1)];
+  __shared__ float s_lsed;
+  DraftRow<D, (TM > 0 ? TM : 1)> dr;
+  if constexpr (TM > 0) {
+    if (wv == 0) draft_row_load(dr, a.q, a.kd, a.vd, b, t, head, kvh, a.T, a.Hq, a.Hkv, lane);
+  }
 
   // block-wide max / sum of per-thread values through the 4 waves
   auto block_max2 = [&](float& x, float& y) {
@@ -1069,9 +1085,22 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   __syncthreads();
 
   const RowCombine cb = combine_row(M, MF, Ls, ZF, ZFa, alpha, a.beta, a.fold_variant);
-  const int32_t t = row / a.G;
-  const int32_t head = kvh * a.G + (row - t * a.G);
-  const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
+  float lse_out = cb.lse;
+  DraftMerge mg{1.f, 0.f, cb.lse};
+  if constexpr (TM > 0) {
+    if (wv == 0) {
+      const int32_t L = a.seqs.nseq > 0 ? a.seqs.len[b] : a.ctx_len[b];
+      const float c = draft_logit_scale(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
+      float lse_d, od[D / 64];
+      draft_row_part(dr, t, c, lse_d, od);
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) s_od[lane * (D / 64) + e] = od[e];
+      if (lane == 0) s_lsed = lse_d;
+    }
+    __syncthreads();
+    mg = draft_merge(cb.lse, s_lsed);
+    lse_out = mg.lse;
+  }
   // Final combine: thread c < D owns output channel c.
   if (tid < D) {
     const float* pm = (const float*)&s_part[0][0][0];
@@ -1082,11 +1111,14 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
       sm += pm[g2 * D + tid];
       sf += pf[g2 * D + tid];
     }
-    const float res = sm * cb.fl + sf * cb.ff;
+    // explicit fmaf: the separate merge call reads this value back and must
+    // see the same rounding as the fused merge below
+    float res = fmaf(sm, cb.fl, sf * cb.ff);
+    if constexpr (TM > 0) res = draft_merge_out(mg, res, s_od[tid]);
     if (a.out_bf16) ((__bf16*)a.out)[orow * D + tid] = (__bf16)res;
     else ((float*)a.out)[orow * D + tid] = res;
   }
-  if (tid == 0) a.lse[orow] = cb.lse;
+  if (tid == 0) a.lse[orow] = lse_out;
 }
 
 // ---------------------------------------------------------------- launch
@@ -1104,14 +1136,24 @@ static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t 
 
 }  // namespace da
 
-extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
-                                 const void* v_cache, const void* k_side, const int32_t* block_table,
-                                 const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
-                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace da;
+namespace da {
+
+// The decode call, optionally fused with the draft part (kd, vd non-null).
+static int decode_impl(const draft_attn_params* p, const void* q, const void* k_cache, const void* v_cache,
+                       const void* k_side, const int32_t* block_table, const int32_t* ctx_len_dev,
+                       const int32_t* ctx_len_host, const void* kd, const void* vd, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pr;
   const int st = prepare(p, ctx_len_host, &pr);
   if (st != DRAFT_ATTN_OK) return st;
+  const bool fused = kd != nullptr;
+  if (fused) {
+    // The draft part is applied by the merge kernel, so the call always runs
+    // on two kernels (the layout of the workspace does not depend on it).
+    pr.single = false;
+    if (!vd) return DRAFT_ATTN_EINVAL;
+    if (((uintptr_t)kd & 15) != 0 || ((uintptr_t)vd & 15) != 0) return DRAFT_ATTN_EINVAL;
+  }
   if ((p->prof_events[0] == nullptr) != (p->prof_events[1] == nullptr)) return DRAFT_ATTN_EINVAL;
   if (p->num_seqs == 0) return DRAFT_ATTN_OK;
   if (!q || !k_cache || !v_cache || !block_table || !ctx_len_dev || !out || !lse || !workspace)
@@ -1206,6 +1248,12 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   a2.fold_variant = p->fold_variant;
   a2.out_bf16 = a1.out_bf16;
   a2.seqs = a1.seqs;
+  a2.q = (const __bf16*)q;
+  a2.kd = (const __bf16*)kd;
+  a2.vd = (const __bf16*)vd;
+  a2.n0 = p->n0;
+  a2.kappa = p->kappa;
+  a2.scale = p->softmax_scale;
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();  // clear a stale error so the check below reports ours
@@ -1228,9 +1276,41 @@ extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, cons
   if (p->prof_events[1]) (void)hipEventRecord((hipEvent_t)p->prof_events[1], s);
   if (!single) {
     const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
-    if (D == 64) pass2_kernel<64><<<rows_total, 256, 0, s>>>(a2);
-    else pass2_kernel<128><<<rows_total, 256, 0, s>>>(a2);
+    // TM: draft keys 0..TM-1 held in registers, the smallest of 8, 16 and 32
+    // that covers T (T <= 32 since G * T <= 32).
+    const int tm = !fused ? 0 : (a2.T <= 8 ? 8 : (a2.T <= 16 ? 16 : 32));
+    if (D == 64) {
+      if (tm == 0) pass2_kernel<64, 0><<<rows_total, 256, 0, s>>>(a2);
+      else if (tm == 8) pass2_kernel<64, 8><<<rows_total, 256, 0, s>>>(a2);
+      else if (tm == 16) pass2_kernel<64, 16><<<rows_total, 256, 0, s>>>(a2);
+      else pass2_kernel<64, 32><<<rows_total, 256, 0, s>>>(a2);
+    } else {
+      if (tm == 0) pass2_kernel<128, 0><<<rows_total, 256, 0, s>>>(a2);
+      else if (tm == 8) pass2_kernel<128, 8><<<rows_total, 256, 0, s>>>(a2);
+      else if (tm == 16) pass2_kernel<128, 16><<<rows_total, 256, 0, s>>>(a2);
+      else pass2_kernel<128, 32><<<rows_total, 256, 0, s>>>(a2);
+    }
   }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
+}
+
+}  // namespace da
+
+extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
+                                 const void* v_cache, const void* k_side, const int32_t* block_table,
+                                 const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return da::decode_impl(p, q, k_cache, v_cache, k_side, block_table, ctx_len_dev, ctx_len_host, nullptr, nullptr,
+                         out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int draft_attn_decode_draft(const draft_attn_params* p, const void* q, const void* k_cache,
+                                       const void* v_cache, const void* k_side, const int32_t* block_table,
+                                       const int32_t* ctx_len_dev, const int32_t* ctx_len_host,
+                                       const void* k_draft, const void* v_draft, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_draft || !v_draft) return DRAFT_ATTN_EINVAL;
+  return da::decode_impl(p, q, k_cache, v_cache, k_side, block_table, ctx_len_dev, ctx_len_host, k_draft, v_draft,
+                         out, lse, workspace, workspace_bytes, stream);
 }

@@ -15,6 +15,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "draft_part.h"
 #include "host.h"
 #include "plan.h"
 
@@ -31,17 +32,11 @@ struct MergeArgs {
   float kappa, scale;
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 // One wave per (sequence, draft token, query head); lane l owns channels
 // l*CPL .. l*CPL + CPL - 1. Every load the wave needs (its query row, the cache
 // result, draft keys and values 0..t) is issued before any is used, so the call
 // costs about one memory round trip; the logits are then reduced across the
-// wave one draft key at a time.
+// wave one draft key at a time (draft_part.h).
 template <int D, int TM>
 __global__ __launch_bounds__(64) void merge_draft_kernel(const MergeArgs a) {
   constexpr int CPL = D / 64;
@@ -54,65 +49,21 @@ __global__ __launch_bounds__(64) void merge_draft_kernel(const MergeArgs a) {
   const int32_t kvh = h / a.G;
   const int64_t qrow = ((int64_t)b * a.T + t) * a.Hq + h;
 
-  float qv[CPL], oc[CPL];
-  float kx[TM][CPL], vx[TM][CPL];
+  DraftRow<D, TM> dr;
+  draft_row_load(dr, a.q, a.kd, a.vd, b, t, h, kvh, a.T, a.Hq, a.Hkv, lane);
+  float oc[CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    qv[e] = (float)a.q[qrow * D + lane * CPL + e];
-    oc[e] = a.out[qrow * D + lane * CPL + e];
-  }
+  for (int e = 0; e < CPL; ++e) oc[e] = a.out[qrow * D + lane * CPL + e];
   const float lse_c = a.lse[qrow];
-  // Loads are unconditional, from row min(j, t): a load under a condition makes
-  // the compiler wait for it before the branch joins.
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int32_t jc = j <= t ? j : t;
-    const int64_t row = (((int64_t)b * a.T + jc) * a.Hkv + kvh) * D + lane * CPL;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      kx[j][e] = (float)a.kd[row + e];
-      vx[j][e] = (float)a.vd[row + e];
-    }
-  }
-  const int32_t n = visible_count(a.ctx_len[b], a.mode, a.W, a.S);
-  const double sn = 1.0 + (double)a.kappa * log((double)(n > a.n0 ? n : a.n0) / (double)a.n0);
-  const float c = (float)((double)a.scale * sn);
-
-  float lg[TM];
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    lg[j] = -INFINITY;
-    if (j <= t) {
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) part += qv[e] * kx[j][e];
-      lg[j] = c * wave_sum(part);
-      m = fmaxf(m, lg[j]);
-    }
-  }
-  float z = 0.f, od[CPL];
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) od[e] = 0.f;
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    if (j <= t) {
-      const float pj = expf(lg[j] - m);
-      z += pj;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) od[e] += pj * vx[j][e];
-    }
-  }
-  const float lse_d = m + logf(z);
-  const float top = fmaxf(lse_c, lse_d);
-  const float wc = expf(lse_c - top), wd = expf(lse_d - top);
-  const float den = wc + wd;
+  const float c = draft_logit_scale(a.scale, a.kappa, visible_count(a.ctx_len[b], a.mode, a.W, a.S), a.n0);
+  float lse_d, od[CPL];
+  draft_row_part(dr, t, c, lse_d, od);
+  const DraftMerge mg = draft_merge(lse_c, lse_d);
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
-    const float o = wc > 0.f ? oc[e] : 0.f;
-    a.out[qrow * D + lane * CPL + e] = (wc * o + wd * od[e] / z) / den;
+    a.out[qrow * D + lane * CPL + e] = draft_merge_out(mg, oc[e], od[e]);
   }
-  if (lane == 0) a.lse[qrow] = top + logf(den);
+  if (lane == 0) a.lse[qrow] = mg.lse;
 }
 
 }  // namespace da

@@ -67,3 +67,40 @@ def test_prepared_merge_draft_matches_the_direct_call():
     call()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mode="full"),
+    dict(mode="window", window=500, n_sink=4),
+    dict(mode="fold", window=700, alpha=2.0, beta=-1.0),
+    dict(mode="fold", window=300, alpha=4.0, beta=0.5, kappa=0.1, n0=64, rope="none"),
+], ids=["full", "window", "fold", "fold-kappa-nope"])
+@pytest.mark.parametrize("d,T,G", [(128, 4, 4), (64, 8, 2), (128, 1, 8), (128, 32, 1), (64, 12, 2)])
+def test_fused_decode_draft_equals_the_two_calls(kw, d, T, G):
+    # draft_attn_decode_draft applies the draft part inside the decode's merge
+    # kernel with the same arithmetic as the separate merge call: fp32 results
+    # equal bit for bit, on either launch setting (the fused call always runs on
+    # two kernels), and bf16 output is the fused fp32 value rounded once.
+    import draft_attention_amd as da
+    dev = torch.device("cuda:0")
+    lens = [0, 5, 3000, 1234]
+    Hkv = 2
+    x = synth.make_inputs(ctx_lens=lens, T=T, Hq=G * Hkv, Hkv=Hkv, d=d, seed=71, fold=True)
+    g = torch.Generator().manual_seed(72)
+    kd = (torch.randn((4, T, Hkv, d), generator=g) * 2).to(torch.bfloat16).to(dev)
+    vd = torch.randn((4, T, Hkv, d), generator=g).to(torch.bfloat16).to(dev)
+    q, kc, vc, ks = (x[k].to(dev) for k in ("q", "k_cache", "v_cache", "k_side"))
+    table, ctx = x["block_table"].to(dev), x["ctx_len"].to(dev)
+    side = ks if kw["mode"] == "fold" else None
+    out, lse = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, launch="two_pass", **kw)
+    da.merge_draft(q, kd, vd, ctx, out, lse, num_blocks=kc.shape[0], max_blocks_per_seq=table.shape[1],
+                   num_kv_heads=Hkv, ctx_lens=lens, rope_theta=5e5, **kw)
+    for launch in ("auto", "single"):
+        fo, fl = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, launch=launch,
+                           k_draft=kd, v_draft=vd, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(fo, out) and torch.equal(fl, lse), (kw, launch)
+    bo, bl = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, out_dtype="bf16",
+                       k_draft=kd, v_draft=vd, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bo, out.to(torch.bfloat16)) and torch.equal(bl, lse)
