@@ -345,8 +345,8 @@ def test_full_size_batch16_ragged():
         _sampled(w, kw, pairs=[(0, 2), (7, 2), (15, 6)])
 
 
-@pytest.mark.parametrize("launch", ["two_pass", "single"])
-def test_graph_replay_matches_eager(launch):
+@pytest.mark.parametrize("launch,fused", [("two_pass", False), ("single", False), ("auto", True)])
+def test_graph_replay_matches_eager(launch, fused):
     # The call captured in a HIP graph, replayed several times with eager work in
     # between; every replay must equal the eager result bit for bit. A
     # workspace filled with garbage before a replay must not matter.
@@ -359,10 +359,15 @@ def test_graph_replay_matches_eager(launch):
     p = da.make_params(num_seqs=2, num_draft_tokens=4, num_q_heads=16, num_kv_heads=4, head_dim=128,
                        num_blocks=g["k_cache"].shape[0], max_blocks_per_seq=g["block_table"].shape[1], **kw)
     ws = torch.empty(da.workspace_size(p, g["ctx_lens"]), dtype=torch.uint8, device="cuda:0")
+    # fused: the call with the step's draft keys (draft_attn_decode_draft)
+    gen = torch.Generator(device="cuda:0").manual_seed(22)
+    kd = torch.randn((2, 4, 4, 128), generator=gen, device="cuda:0").to(torch.bfloat16) if fused else None
+    vd = torch.randn((2, 4, 4, 128), generator=gen, device="cuda:0").to(torch.bfloat16) if fused else None
 
     def call():
         da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=g["k_side"],
-                  ctx_lens=g["ctx_lens"], out=out, lse=lse, workspace=ws, rope_theta=5e5, launch=launch, **kw)
+                  ctx_lens=g["ctx_lens"], out=out, lse=lse, workspace=ws, rope_theta=5e5, launch=launch,
+                  k_draft=kd, v_draft=vd, **kw)
 
     call()
     torch.cuda.synchronize()
