@@ -421,6 +421,21 @@ def test_merge_draft_refuses_bf16_output():
     assert st == -4
 
 
+def test_fused_decode_draft_validates_the_draft_pointers():
+    # Checked on the host before anything is enqueued (no GPU needed): both
+    # draft pointers are required and must be 16-byte aligned.
+    p = params()
+    host = (ctypes.c_int32 * 2)(*LENS)
+    f = da().lib.draft_attn_decode_draft
+    common = (0x10000, 0x20000, 0x30000, None, 0x40000, 0x50000, host)
+    tail = (0x80000, 0x90000, 0x100000, 1, None)   # a 1-byte workspace: ENOSPC once everything else passes
+    assert f(ctypes.byref(p), *common, None, None, *tail) == -1
+    assert f(ctypes.byref(p), *common, 0x60000, None, *tail) == -1
+    assert f(ctypes.byref(p), *common, 0x60008, 0x70000, *tail) == -1
+    assert f(ctypes.byref(p), *common, 0x60000, 0x70004, *tail) == -1
+    assert f(ctypes.byref(p), *common, 0x60000, 0x70000, *tail) == -2
+
+
 # ----------------------------------------------------------------------------- binding argument checks
 def test_binding_rejects_host_tensors_and_wrong_dtypes():
     # These checks run before any GPU call, so they are safe without a GPU.
