@@ -81,6 +81,9 @@ struct Pass1Args {
   uint8_t* visit;    // optional [B][visit_stride]
   int64_t visit_stride;
   unsigned long long* flags;  // [items] done flags (single launch)
+  const __bf16* kd;  // fused call only: draft keys / values [B][T][Hkv][D] (else null)
+  const __bf16* vd;
+  float* dpart;      // fused call: draft parts, out_d [B*T*Hq][D] then lse_d [B*T*Hq]
   void* out;         // [B][T][Hq][D] fp32 or bf16 (single launch)
   float* lse;        // [B][T][Hq] (single launch)
   int32_t B, T, Hq, Hkv, G, R, rows_pad, max_blocks, num_blocks;
@@ -97,9 +100,10 @@ struct Pass2Args {
   const int32_t* ctx_len;
   void* out;
   float* lse;
-  const __bf16* q;   // draft part (fused call only): query rows [B][T][Hq][D]
-  const __bf16* kd;  // draft keys [B][T][Hkv][D], rotated at the draft positions
-  const __bf16* vd;  // draft values [B][T][Hkv][D]
+  const float* dpart;  // fused call, T <= 8: draft parts written by pass 1 (out_d rows, then lse_d)
+  const __bf16* q;     // fused call, T > 8: the draft part's inputs
+  const __bf16* kd;
+  const __bf16* vd;
   int32_t B, T, Hq, Hkv, G, R, rows_pad;
   int32_t mode, W, S, C, total_items, fold_variant, out_bf16, n0;
   float alpha, beta, kappa, scale;
@@ -665,6 +669,23 @@ __device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int3
   }
 }
 
+// Fused call: the draft part of query row r = (b * T + t) * Hq + h, formed by
+// one wave of an extra pass-1 workgroup and stored for the merge kernel.
+template <int D, int TM>
+__device__ __forceinline__ void draft_part_store(const Pass1Args& a, int32_t r, int lane) {
+  const int32_t h = r % a.Hq, bt = r / a.Hq;
+  const int32_t t = bt % a.T, b = bt / a.T;
+  DraftRow<D, TM> dr;
+  draft_row_load(dr, a.q, a.kd, a.vd, b, t, h, h / a.G, a.T, a.Hq, a.Hkv, lane);
+  const int32_t L = a.seqs.nseq > 0 ? a.seqs.len[b] : a.ctx_len[b];
+  const float c = draft_logit_scale(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
+  float lse_d, od[D / 64];
+  draft_row_part(dr, t, c, lse_d, od);
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) a.dpart[(int64_t)r * D + lane * (D / 64) + e] = od[e];
+  if (lane == 0) a.dpart[(int64_t)a.B * a.T * a.Hq * D + r] = lse_d;
+}
+
 // Waves per SIMD, i.e. workgroups per CU, that the kernel is compiled for; the
 // host planner's resident_per_cu() uses the same numbers.
 constexpr int pass1_occupancy(int D, int RT) { return D == 64 ? (RT == 1 ? 3 : 2) : 1; }
@@ -677,6 +698,16 @@ void pass1_kernel(const Pass1Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i16 = lane & 15, g = lane >> 4;
   const int32_t w = blockIdx.x;
   const int32_t rp = a.rows_pad;
+  if (!SINGLE && a.kd != nullptr && w >= a.total_items) {
+    // Fused call: workgroups past the work items form the draft parts, one
+    // query row per wave (they do not depend on the cache part, so the merge
+    // kernel only loads them).
+    // (The host adds these workgroups only for T <= 8: holding 16 or 32 draft
+    // keys here raised the register demand of the whole kernel into spills.)
+    const int32_t r = (w - a.total_items) * kWaves + wave;
+    if (r < a.B * a.T * a.Hq) draft_part_store<D, 8>(a, r, lane);
+    return;
+  }
   int32_t* sbid = (int32_t*)smem;
   float* s_m = (float*)(smem + pass1_sbid_bytes(a.C));  // [kWaves][rp] row maxima
   float2* s_l = (float2*)(s_m + kWaves * rp);           // [kWaves][rp] (acc denominator, plain sum)
@@ -902,11 +933,15 @@ void pass1_kernel(const Pass1Args a) {
 // of them. Longer rows stream the records in tiles.
 constexpr int kFastItems = 8;
 
-// TM > 0: the fused call. Wave 0 also forms the row's draft part (draft keys
-// 0..t of the step, draft_part.h; its loads are issued with the records') and
-// the row is written already merged with it.
-template <int D, int TM>
+// DM != 0: the fused call; the row is written already merged with its draft
+// part (draft keys 0..t of the step, draft_part.h). DM == 1: pass 1's extra
+// workgroups formed the part, and it is loaded with the records. DM == 16 or
+// 32 (more than 8 draft tokens): wave 0 forms it here, its loads issued with
+// the records', after the row's reductions.
+template <int D, int DM>
 __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
+  constexpr bool FUSED = DM != 0;
+  constexpr int TM = DM > 1 ? DM : 1;
   constexpr int NQ = D / 4;     // float4 channel quads per row
   constexpr int NG = 256 / NQ;  // item groups
   constexpr int TILE = 1024;    // items whose scales are staged at once (long rows)
@@ -937,10 +972,16 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   const int32_t t = row / a.G;
   const int32_t head = kvh * a.G + (row - t * a.G);
   const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
-  __shared__ float s_od[(TM > 0 ? D : 1)];
+  float od_row = 0.f, lse_d = 0.f;
+  if constexpr (DM == 1) {
+    const int64_t nd = (int64_t)a.B * a.T * a.Hq;
+    od_row = a.dpart[orow * D + (tid < D ? tid : 0)];
+    lse_d = a.dpart[nd * D + orow];
+  }
+  __shared__ float s_od[DM > 1 ? D : 1];
   __shared__ float s_lsed;
-  DraftRow<D, (TM > 0 ? TM : 1)> dr;
-  if constexpr (TM > 0) {
+  DraftRow<D, TM> dr;
+  if constexpr (DM > 1) {
     if (wv == 0) draft_row_load(dr, a.q, a.kd, a.vd, b, t, head, kvh, a.T, a.Hq, a.Hkv, lane);
   }
 
@@ -1087,18 +1128,22 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   const RowCombine cb = combine_row(M, MF, Ls, ZF, ZFa, alpha, a.beta, a.fold_variant);
   float lse_out = cb.lse;
   DraftMerge mg{1.f, 0.f, cb.lse};
-  if constexpr (TM > 0) {
+  if constexpr (DM > 1) {
     if (wv == 0) {
       const int32_t L = a.seqs.nseq > 0 ? a.seqs.len[b] : a.ctx_len[b];
       const float c = draft_logit_scale(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
-      float lse_d, od[D / 64];
-      draft_row_part(dr, t, c, lse_d, od);
+      float ld, od[D / 64];
+      draft_row_part(dr, t, c, ld, od);
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) s_od[lane * (D / 64) + e] = od[e];
-      if (lane == 0) s_lsed = lse_d;
+      if (lane == 0) s_lsed = ld;
     }
     __syncthreads();
-    mg = draft_merge(cb.lse, s_lsed);
+    if (tid < D) od_row = s_od[tid];
+    lse_d = s_lsed;
+  }
+  if constexpr (FUSED) {
+    mg = draft_merge(cb.lse, lse_d);
     lse_out = mg.lse;
   }
   // Final combine: thread c < D owns output channel c.
@@ -1114,7 +1159,7 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
     // explicit fmaf: the separate merge call reads this value back and must
     // see the same rounding as the fused merge below
     float res = fmaf(sm, cb.fl, sf * cb.ff);
-    if constexpr (TM > 0) res = draft_merge_out(mg, res, s_od[tid]);
+    if constexpr (FUSED) res = draft_merge_out(mg, res, od_row);
     if (a.out_bf16) ((__bf16*)a.out)[orow * D + tid] = (__bf16)res;
     else ((float*)a.out)[orow * D + tid] = res;
   }
@@ -1180,6 +1225,10 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   a1.visit = p->debug_visit;
   a1.visit_stride = p->debug_visit_stride;
   a1.flags = (unsigned long long*)(ws + pr.flag_offset);
+  // pass 1 forms the draft parts only for T <= 8 (see draft_wgs below)
+  a1.kd = kd != nullptr && p->num_draft_tokens <= 8 ? (const __bf16*)kd : nullptr;
+  a1.vd = a1.kd != nullptr ? (const __bf16*)vd : nullptr;
+  a1.dpart = (float*)(ws + pr.draft_offset);
   a1.out = out;
   a1.lse = lse;
   a1.out_bf16 = p->out_dtype == DRAFT_ATTN_OUT_BF16;
@@ -1248,6 +1297,7 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   a2.fold_variant = p->fold_variant;
   a2.out_bf16 = a1.out_bf16;
   a2.seqs = a1.seqs;
+  a2.dpart = a1.dpart;
   a2.q = (const __bf16*)q;
   a2.kd = (const __bf16*)kd;
   a2.vd = (const __bf16*)vd;
@@ -1261,10 +1311,16 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   // Every (sequence, kv head) has at least one item, so the single kernel
   // writes every output row.
   const bool single = pr.single && pr.total_items > 0;
-  if (pr.total_items > 0) {
+  // the fused call adds one workgroup per four query rows for the draft parts
+  // (T <= 8: for more draft tokens the merge kernel forms the parts itself)
+  const bool draft_in_pass1 = fused && p->num_draft_tokens <= 8;
+  const int64_t draft_wgs =
+      draft_in_pass1 ? ((int64_t)p->num_seqs * p->num_draft_tokens * p->num_q_heads + kWaves - 1) / kWaves : 0;
+  if (pr.total_items + draft_wgs > 0x7fffffff) return DRAFT_ATTN_EINVAL;
+  if (pr.total_items + draft_wgs > 0) {
     const size_t lds = pass1_lds_bytes(pr.chunk, pr.rows_pad, D);
     const bool fold = p->mode == kFold;
-    const uint32_t grid = (uint32_t)pr.total_items;
+    const uint32_t grid = (uint32_t)(pr.total_items + draft_wgs);
     if (single) {
       if (D == 64) launch_pass1<64, true>(a1, pr.row_tiles, fold, grid, lds, s);
       else launch_pass1<128, true>(a1, pr.row_tiles, fold, grid, lds, s);
@@ -1276,18 +1332,16 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   if (p->prof_events[1]) (void)hipEventRecord((hipEvent_t)p->prof_events[1], s);
   if (!single) {
     const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
-    // TM: draft keys 0..TM-1 held in registers, the smallest of 8, 16 and 32
-    // that covers T (T <= 32 since G * T <= 32).
-    const int tm = !fused ? 0 : (a2.T <= 8 ? 8 : (a2.T <= 16 ? 16 : 32));
+    const int dm = !fused ? 0 : (draft_in_pass1 ? 1 : (a2.T <= 16 ? 16 : 32));
     if (D == 64) {
-      if (tm == 0) pass2_kernel<64, 0><<<rows_total, 256, 0, s>>>(a2);
-      else if (tm == 8) pass2_kernel<64, 8><<<rows_total, 256, 0, s>>>(a2);
-      else if (tm == 16) pass2_kernel<64, 16><<<rows_total, 256, 0, s>>>(a2);
+      if (dm == 0) pass2_kernel<64, 0><<<rows_total, 256, 0, s>>>(a2);
+      else if (dm == 1) pass2_kernel<64, 1><<<rows_total, 256, 0, s>>>(a2);
+      else if (dm == 16) pass2_kernel<64, 16><<<rows_total, 256, 0, s>>>(a2);
       else pass2_kernel<64, 32><<<rows_total, 256, 0, s>>>(a2);
     } else {
-      if (tm == 0) pass2_kernel<128, 0><<<rows_total, 256, 0, s>>>(a2);
-      else if (tm == 8) pass2_kernel<128, 8><<<rows_total, 256, 0, s>>>(a2);
-      else if (tm == 16) pass2_kernel<128, 16><<<rows_total, 256, 0, s>>>(a2);
+      if (dm == 0) pass2_kernel<128, 0><<<rows_total, 256, 0, s>>>(a2);
+      else if (dm == 1) pass2_kernel<128, 1><<<rows_total, 256, 0, s>>>(a2);
+      else if (dm == 16) pass2_kernel<128, 16><<<rows_total, 256, 0, s>>>(a2);
       else pass2_kernel<128, 32><<<rows_total, 256, 0, s>>>(a2);
     }
   }

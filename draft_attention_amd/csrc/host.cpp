@@ -216,13 +216,17 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
   out->rows_pad = rows_pad;
   out->single = single;
   out->max_group_items = gmax;
-  // Layout: [one 64-bit done flag per item] [stat] [acc]. The flags are
+  // Layout: [one 64-bit done flag per item] [stat] [acc] [draft parts]. The flags are
   // reserved on both paths so the layout does not depend on the launch shape.
   const size_t nrows = (size_t)items * (size_t)rows_pad;
   out->flag_offset = 0;
   out->stat_offset = align_up((size_t)items * sizeof(uint64_t), 256);
   out->acc_offset = out->stat_offset + align_up(nrows * 4 * sizeof(float), 256);
-  out->workspace_bytes = align_up(out->acc_offset + nrows * (size_t)p->head_dim * sizeof(float), 256);
+  // [draft parts] of draft_attn_decode_draft, reserved on every call so that
+  // one workspace size serves both calls: B*T*Hq rows of d + 1 floats.
+  out->draft_offset = out->acc_offset + align_up(nrows * (size_t)p->head_dim * sizeof(float), 256);
+  const size_t drows = (size_t)B * T * Hq;
+  out->workspace_bytes = align_up(out->draft_offset + drows * ((size_t)p->head_dim + 1) * sizeof(float), 256);
   if (out->workspace_bytes == 0) out->workspace_bytes = 256;
   return DRAFT_ATTN_OK;
 }

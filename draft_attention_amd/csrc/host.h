@@ -21,6 +21,7 @@ struct Prepared {
   size_t flag_offset;     // workspace offset of the per-item 64-bit done flags
   size_t stat_offset;     // workspace offset of the per-row statistics
   size_t acc_offset;      // workspace offset of the per-row partial outputs
+  size_t draft_offset;    // workspace offset of the fused call's draft parts: out_d [B*T*Hq][d], then lse_d [B*T*Hq]
   size_t workspace_bytes; // bytes the call needs
 };
 
