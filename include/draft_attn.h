@@ -274,12 +274,15 @@ int draft_attn_merge_draft(const draft_attn_params* p, const void* q, const void
 /* draft_attn_decode and draft_attn_merge_draft in one call: the cache
  * attention of the step, already merged with the draft part (same definitions
  * and arguments as those two calls; k_draft, v_draft as for merge_draft,
- * non-NULL). The merge kernel of the decode applies the draft part to each row
- * before writing it, so the call runs on two kernels whatever `launch` says, saves
- * the separate merge launch, and may write out in bf16 (rounded once, from the
+ * non-NULL, 16-byte aligned). With up to 8 draft tokens, extra workgroups of the
+ * streaming kernel form the draft parts beside the cache pass; with more, the
+ * merge kernel forms them. Either way the merge kernel writes each row already
+ * merged, so the call runs on two kernels whatever `launch` says, saves the
+ * separate merge launch, and may write out in bf16 (rounded once, from the
  * merged fp32 value). With out_dtype F32 the results equal those of the two
  * calls bit for bit. Errors as for draft_attn_decode; the workspace is sized by
- * draft_attn_workspace_size with the same params. */
+ * draft_attn_workspace_size with the same params (it always reserves the draft
+ * parts, B * T * Hq * (d + 1) floats). */
 int draft_attn_decode_draft(const draft_attn_params* p, const void* q, const void* k_cache,
                             const void* v_cache, const void* k_side, const int32_t* block_table,
                             const int32_t* ctx_len_dev, const int32_t* ctx_len_host, const void* k_draft,
