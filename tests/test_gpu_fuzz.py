@@ -42,8 +42,12 @@ def draw(rnd):
     launch = rnd.choice(["auto", "two_pass", "single"])
     out_dtype = rnd.choice(["f32", "f32", "bf16"])
     needle = rnd.choice([0.0, 0.0, 0.02])
+    # drawn last, so the earlier fields of every case stay as they were: about a
+    # quarter of the cases take the fused call with the step's draft keys (the
+    # oracle's draft reference covers FOLD's default reading only)
+    fused = rnd.random() < 0.25 and kw.get("fold_variant", "B") == "B"
     return dict(d=d, Hkv=Hkv, G=G, T=T, lens=lens, kw=kw, split=split, launch=launch, out_dtype=out_dtype,
-                needle=needle)
+                needle=needle, fused=fused)
 
 
 CASES = [draw(random.Random(1000 + i)) for i in range(N_CASES)]
@@ -60,10 +64,17 @@ def test_random_configuration_matches_the_oracle(case):
     stride = max(max(c["lens"]), 1)
     vis = torch.zeros((len(c["lens"]), stride), dtype=torch.uint8, device=dev)
     side = g["k_side"] if c["kw"]["mode"] == "fold" else None
+    kd = vd = None
+    if c["fused"]:
+        gen = torch.Generator().manual_seed(hash((c["d"], c["T"], tuple(c["lens"]))) % (1 << 31))
+        kd = (torch.randn((len(c["lens"]), c["T"], c["Hkv"], c["d"]), generator=gen) * 2).to(torch.bfloat16)
+        vd = torch.randn((len(c["lens"]), c["T"], c["Hkv"], c["d"]), generator=gen).to(torch.bfloat16)
     try:
         out, lse = da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"], k_side=side,
                              ctx_lens=c["lens"], rope_theta=5e5, split_keys=c["split"], launch=c["launch"],
-                             out_dtype=c["out_dtype"], debug_visit=vis, **c["kw"])
+                             out_dtype=c["out_dtype"], debug_visit=vis,
+                             k_draft=None if kd is None else kd.to(dev), v_draft=None if vd is None else vd.to(dev),
+                             **c["kw"])
     except da.DraftAttnError as e:
         # the only refusal a valid draw can meet: single launch with a fixed chunk
         # that leaves more than MAX_GROUP_ITEMS items in a group
@@ -71,8 +82,14 @@ def test_random_configuration_matches_the_oracle(case):
         return
     torch.cuda.synchronize()
     n = {k: (v.float().numpy() if torch.is_tensor(v) and v.is_floating_point() else v) for k, v in x.items()}
-    ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), c["lens"], k_side=n["k_side"],
-                        rope_theta=5e5, **c["kw"])
+    if kd is None:
+        ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), c["lens"],
+                            k_side=n["k_side"], rope_theta=5e5, **c["kw"])
+    else:
+        kw = {k: v for k, v in c["kw"].items() if k not in ("mode", "fold_variant")}
+        ref = oracle.decode_with_draft(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), c["lens"],
+                                       c["kw"]["mode"], kd.float().numpy(), vd.float().numpy(), k_side=n["k_side"],
+                                       rope_theta=5e5, **kw)
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
     empty = np.isneginf(ref["lse"])
@@ -81,6 +98,7 @@ def test_random_configuration_matches_the_oracle(case):
     dout = np.abs(o - ref["out"])
     dlse = float(np.abs(l[~empty] - ref["lse"][~empty]).max()) if (~empty).any() else 0.0
     print(f"{c['kw']} d={c['d']} G={c['G']} T={c['T']} lens={c['lens']} split={c['split']} {c['launch']} "
+          f"{'fused ' if c['fused'] else ''}"
           f"{c['out_dtype']}: max|dout|={float(dout.max()) if dout.size else 0:.2e} max|dlse|={dlse:.2e}", flush=True)
     assert np.all(np.isfinite(o)) and np.all(dout <= bound) and dlse <= 1e-3, c
     want = np.zeros_like(vis.cpu().numpy())
