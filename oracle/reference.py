@@ -148,6 +148,14 @@ def _logsumexp(x: np.ndarray) -> np.ndarray:
     return m + np.log(np.exp(x - m[..., None]).sum(axis=-1))
 
 
+def _far_log_mass(fold_variant: str, alpha: float, beta: float, lse_F, lse_Fa):
+    """Log of the far memory's total weight against the local window's Z_L, per
+    reading of FOLD's alpha/beta [FOLD, abstract: the far memory's total weight is
+    controlled apart from the sharpening inside it]: "B" beta + ln Z_F (default),
+    "A" beta + ln Z_Fa (joint softmax), "B'" beta + ln(Z_Fa)/alpha (one virtual key)."""
+    return {"B": beta + lse_F, "A": beta + lse_Fa, "B'": beta + lse_Fa / alpha}[fold_variant]
+
+
 def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int = 0,
            n_sink: int = 0, alpha: float = 1.0, beta: float = 0.0, kappa: float = 0.0,
            n0: int = 1, softmax_scale: float | None = None, rope: str = "neox",
@@ -197,7 +205,7 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, mode: str, *, window: int 
                 lse_F = _logsumexp(phi)
                 lse_Fa = _logsumexp(alpha * phi)
                 # log of the far memory's total weight, per parameterisation
-                far_mass = {"B": beta + lse_F, "A": beta + lse_Fa, "B'": beta + lse_Fa / alpha}[fold_variant]
+                far_mass = _far_log_mass(fold_variant, alpha, beta, lse_F, lse_Fa)
                 tot = np.logaddexp(lse_L, far_mass)
                 with np.errstate(invalid="ignore"):  # -inf - -inf only when a partition is empty
                     w_loc = np.exp(logits - tot[:, None])
@@ -279,15 +287,17 @@ def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, rope: 
 def decode_with_draft(q, k_cache, v_cache, block_table, ctx_len, mode: str, k_draft, v_draft, *,
                       window: int = 0, n_sink: int = 0, alpha: float = 1.0, beta: float = 0.0,
                       kappa: float = 0.0, n0: int = 1, softmax_scale: float | None = None,
-                      rope: str = "neox", rope_theta: float = 1e4, k_side=None):
+                      rope: str = "neox", rope_theta: float = 1e4, k_side=None, fold_variant: str = "B"):
     """Cache attention plus causal attention among the draft tokens, as one softmax.
 
     Draft token t of sequence b also attends to the step's own draft keys
     k_draft[b, 0..t] (already rotated at their positions L_b + t'), which are not
     in the cache yet. They sit at exact positions next to the window, so for FOLD
-    they join the local partition. Reading (no page states it): their logits use
-    the same scale c = softmax_scale * s(n) as the cached keys, with n the
-    cached visible count. q: [B, T, Hq, d]; k_draft, v_draft: [B, T, Hkv, d].
+    they join the local partition, and the far memory's log-weight is that of
+    the chosen reading (``fold_variant``, as in ``decode``). Reading (no page
+    states it): their logits use the same scale c = softmax_scale * s(n) as the
+    cached keys, with n the cached visible count. q: [B, T, Hq, d]; k_draft,
+    v_draft: [B, T, Hkv, d].
     """
     q = np.asarray(q, dtype=np.float64)
     kd = np.asarray(k_draft, dtype=np.float64)
@@ -318,9 +328,10 @@ def decode_with_draft(q, k_cache, v_cache, block_table, ctx_len, mode: str, k_dr
                     Qf = rope_rotate(Q, -(L - int(window) - 1), rope_theta) if rope == "neox" else Q
                     phi = c * (Qf @ U.T)
                     lse_L, lse_F, lse_Fa = _logsumexp(logits), _logsumexp(phi), _logsumexp(alpha * phi)
-                    tot = np.logaddexp(lse_L, beta + lse_F)
+                    mass = _far_log_mass(fold_variant, alpha, beta, lse_F, lse_Fa)
+                    tot = np.logaddexp(lse_L, mass)
                     with np.errstate(invalid="ignore"):
-                        w_far = np.exp(beta + lse_F - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])
+                        w_far = np.exp(mass - tot)[:, None] * np.exp(alpha * phi - lse_Fa[:, None])
                     o = np.exp(logits - tot[:, None]) @ Vm + (w_far @ Vf if far.size else 0.0)
                 else:
                     tot = _logsumexp(logits)

@@ -21,8 +21,8 @@ MUTATIONS = [
     ("rope frequency exponent", "omega = float(theta) ** (-2.0 * np.arange(h", "omega = float(theta) ** (-1.0 * np.arange(h"),
     ("rope pair sign", "x1 * sin + x2 * cos], axis=-1)", "x1 * sin - x2 * cos], axis=-1)"),
     ("rope pairs adjacent channels", "x1, x2 = x[..., :h], x[..., h:]", "x1, x2 = x[..., 0::2], x[..., 1::2]"),
-    ("beta dropped", 'far_mass = {"B": beta + lse_F,', 'far_mass = {"B": lse_F,'),
-    ("alpha leaks into the far mass", 'far_mass = {"B": beta + lse_F,', 'far_mass = {"B": beta + lse_Fa,'),
+    ("beta dropped", 'return {"B": beta + lse_F,', 'return {"B": lse_F,'),
+    ("alpha leaks into the far mass", 'return {"B": beta + lse_F,', 'return {"B": beta + lse_Fa,'),
     ("far weights not normalised by Z_Fa", "np.exp(alpha * phi - lse_Fa[:, None])\n                o = w_loc", "np.exp(alpha * phi - lse_F[:, None])\n                o = w_loc"),
     ("variant A with the unsharpened mass", '"A": beta + lse_Fa,', '"A": beta + lse_F,'),
     ("variant B' without the 1/alpha", '"B\'": beta + lse_Fa / alpha}', '"B\'": beta + lse_Fa}'),
@@ -39,6 +39,7 @@ MUTATIONS = [
     ("empty set gives NaN", "if n == 0:\n                o = np.zeros((T * G, d))", "if n == 0:\n                o = np.full((T * G, d), np.nan)"),
     ("bf16 ties away from even", "np.where(lo_even, lo, hi)", "np.where(lo_even, hi, lo)"),
     ("append rotates to p + 1", "rot = bf16_round(rope_rotate(raw, p, rope_theta))", "rot = bf16_round(rope_rotate(raw, p + 1, rope_theta))"),
+    ("draft step ignores the FOLD reading", " mass = _far_log_mass(fold_variant,", ' mass = _far_log_mass("B",'),
     ("draft token sees only earlier drafts", "Km = np.concatenate([K, kd[b, :t + 1, g, :]])", "Km = np.concatenate([K, kd[b, :t, g, :]])"),
 ]
 

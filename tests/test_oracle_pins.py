@@ -588,7 +588,11 @@ def test_draft_tokens_equal_decode_over_the_extended_cache():
     ctx, T, Hkv, G, d = [37, 13], 3, 2, 2, 8        # draft positions L..L+2 stay inside allocated blocks
     k, v, ks, table, q, kd, vd = _draft_inputs(ctx, T, Hkv, G, d, seed=51)
     assert all(table[b, (L + T - 1) // BLOCK] >= 0 for b, L in enumerate(ctx))
-    for mode, kw in (("full", {}), ("window", dict(window=9, n_sink=2)), ("fold", dict(window=9, alpha=2.0, beta=-1.0))):
+    # FOLD under each reading of alpha/beta: the draft keys join the local
+    # partition, so the far memory's log-weight is the reading's own.
+    for mode, kw in (("full", {}), ("window", dict(window=9, n_sink=2)), ("fold", dict(window=9, alpha=2.0, beta=-1.0)),
+                     ("fold", dict(window=9, alpha=2.0, beta=-1.0, fold_variant="A")),
+                     ("fold", dict(window=9, alpha=0.5, beta=0.7, fold_variant="B'"))):
         res = ref.decode_with_draft(q, k, v, table, ctx, mode, kd, vd, k_side=ks, rope_theta=100.0, **kw)
         for b, L in enumerate(ctx):
             for t in range(T):
