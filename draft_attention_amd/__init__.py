@@ -19,7 +19,7 @@ FULL, WINDOW, FOLD = 0, 1, 2
 ROPE_NEOX, ROPE_NONE = 0, 1
 OK, EINVAL, ENOSPC, EHIP, ENOTSUP = 0, -1, -2, -3, -4
 MAX_ROWS = 32
-ABI_VERSION = 3
+ABI_VERSION = 4
 PLAN_ITEM_INTS = 7
 _MODES = {"full": FULL, "window": WINDOW, "fold": FOLD}
 _ROPES = {"neox": ROPE_NEOX, "none": ROPE_NONE}
@@ -30,6 +30,7 @@ _LAUNCHES = {"auto": LAUNCH_AUTO, "two_pass": LAUNCH_TWO_PASS, "single": LAUNCH_
 OUT_F32, OUT_BF16 = 0, 1
 _OUT_DTYPES = {"f32": OUT_F32, "bf16": OUT_BF16}
 MAX_GROUP_ITEMS = 64
+STATUS_BAD_BLOCK, STATUS_LENGTHS, STATUS_APPEND_BAD_BLOCK = 1, 2, 4
 
 
 class Params(ctypes.Structure):
@@ -61,6 +62,7 @@ class Params(ctypes.Structure):
         ("fold_variant", ctypes.c_int32),
         ("launch", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
+        ("status_flags", ctypes.c_void_p),
     ]
 
 
@@ -78,6 +80,7 @@ class AppendParams(ctypes.Structure):
         ("rope", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+        ("status_flags", ctypes.c_void_p),
     ]
 
 
@@ -129,7 +132,7 @@ def _load():
     lib.draft_attn_version.restype = ctypes.c_int
     if lib.draft_attn_version() != ABI_VERSION:
         raise ImportError("libdraft_attn.so ABI version mismatch")
-    if ctypes.sizeof(Params) != 128 or ctypes.sizeof(AppendParams) != 48:
+    if ctypes.sizeof(Params) != 136 or ctypes.sizeof(AppendParams) != 56:
         raise ImportError("params mirror has the wrong size")
     return lib
 
@@ -145,7 +148,7 @@ def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_d
                 max_blocks_per_seq, mode="full", window=0, n_sink=0, alpha=1.0, beta=0.0, kappa=0.0,
                 n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, split_keys=0,
                 debug_visit=0, debug_visit_stride=0, prof_events=None, fold_variant="B", launch="auto",
-                out_dtype="f32") -> Params:
+                out_dtype="f32", status_flags=0) -> Params:
     p = Params()
     lib.draft_attn_params_init(ctypes.byref(p))
     p.num_seqs = int(num_seqs)
@@ -173,6 +176,7 @@ def make_params(*, num_seqs, num_draft_tokens, num_q_heads, num_kv_heads, head_d
     p.out_dtype = _out_code(out_dtype)
     p.debug_visit = int(debug_visit) or None
     p.debug_visit_stride = int(debug_visit_stride)
+    p.status_flags = int(status_flags) or None
     if prof_events is not None:
         p.prof_events[0] = int(prof_events[0])
         p.prof_events[1] = int(prof_events[1])
@@ -285,7 +289,7 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
             beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
             ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
             debug_visit=None, fold_variant="B", launch="auto", out_dtype="f32", k_draft=None,
-            v_draft=None) -> PreparedDecode:
+            v_draft=None, status=None, num_blocks=None) -> PreparedDecode:
     """Marshal the arguments of decode() once (same meaning as there)."""
     import torch
 
@@ -304,12 +308,19 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
     if debug_visit is not None:
         _expect(debug_visit, "debug_visit", torch.uint8, (B, None), dev)
         visit_ptr, visit_stride = debug_visit.data_ptr(), debug_visit.shape[1]
+    status_ptr = 0
+    if status is not None:
+        _expect(status, "status", torch.int32, (1,), dev)
+        status_ptr = status.data_ptr()
+    nb = k_cache.shape[0] if num_blocks is None else int(num_blocks)
+    if nb > k_cache.shape[0]:
+        raise ValueError(f"num_blocks {nb} exceeds the pools' {k_cache.shape[0]} blocks")
     p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
-                    num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
+                    num_blocks=nb, max_blocks_per_seq=block_table.shape[1], mode=mode,
                     window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
                     softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                     split_keys=split_keys, debug_visit=visit_ptr, debug_visit_stride=visit_stride,
-                    fold_variant=fold_variant, launch=launch, out_dtype=out_dtype)
+                    fold_variant=fold_variant, launch=launch, out_dtype=out_dtype, status_flags=status_ptr)
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=_out_torch_dtype(p.out_dtype), device=dev)
     _expect(out, "out", _out_torch_dtype(p.out_dtype), (B, T, Hq, d), dev)
@@ -332,7 +343,8 @@ def prepare(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0,
     else:
         args = (ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_side), ptr(block_table), ptr(ctx_len), host, ptr(out),
                 ptr(lse), ptr(workspace), workspace.numel() * workspace.element_size(), s)
-    keep = (q, k_cache, v_cache, k_side, block_table, ctx_len, workspace, debug_visit, host, k_draft, v_draft)
+    keep = (q, k_cache, v_cache, k_side, block_table, ctx_len, workspace, debug_visit, host, k_draft, v_draft,
+            status)
     return PreparedDecode(p, args, out, lse, keep, fused=fused)
 
 
@@ -340,7 +352,7 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
            beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4, k_side=None,
            ctx_lens=None, out=None, lse=None, workspace=None, stream=None, split_keys=0,
            debug_visit=None, prof_events=None, fold_variant="B", launch="auto", out_dtype="f32",
-           k_draft=None, v_draft=None):
+           k_draft=None, v_draft=None, status=None, num_blocks=None):
     """Enqueue draft_attn_decode on the current (or given) stream; returns (out, lse).
 
     With k_draft / v_draft (bf16 [B,T,Hkv,d], the step's draft keys and values),
@@ -351,13 +363,16 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
     block_table int32 [B,MB]; ctx_len int32 [B] on the device; ctx_lens: the same
     lengths as a host list (read from ctx_len when omitted, which synchronises).
     out / lse / workspace are allocated with torch when not given. launch: "auto",
-    "two_pass" or "single"; out_dtype: "f32" or "bf16" (the dtype of out).
+    "two_pass" or "single"; out_dtype: "f32" or "bf16" (the dtype of out). status: an
+    optional int32 [1] device tensor into which the kernels OR STATUS_* bits (a table
+    entry outside the pool, lengths that disagree); the caller clears it. num_blocks:
+    blocks of the pools the table may name (default: all of them).
     """
     call = prepare(q, k_cache, v_cache, block_table, ctx_len, mode=mode, window=window, n_sink=n_sink, alpha=alpha,
                    beta=beta, kappa=kappa, n0=n0, softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta,
                    k_side=k_side, ctx_lens=ctx_lens, out=out, lse=lse, workspace=workspace, stream=stream,
                    split_keys=split_keys, debug_visit=debug_visit, fold_variant=fold_variant, launch=launch,
-                   out_dtype=out_dtype, k_draft=k_draft, v_draft=v_draft)
+                   out_dtype=out_dtype, k_draft=k_draft, v_draft=v_draft, status=status, num_blocks=num_blocks)
     return call(prof_events=prof_events)
 
 
@@ -385,28 +400,39 @@ def _check_merge(q, k_draft, v_draft, ctx_len, out, lse, num_kv_heads):
 
 
 def make_append_params(*, num_seqs, num_new, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
-                       rope="neox", rope_theta=1e4) -> AppendParams:
+                       rope="neox", rope_theta=1e4, status_flags=0) -> AppendParams:
     p = AppendParams()
     lib.draft_attn_append_params_init(ctypes.byref(p))
     p.num_seqs, p.num_new, p.num_kv_heads, p.head_dim = int(num_seqs), int(num_new), int(num_kv_heads), int(head_dim)
     p.num_blocks, p.max_blocks_per_seq = int(num_blocks), int(max_blocks_per_seq)
     p.rope = _ROPES[rope] if isinstance(rope, str) else int(rope)
     p.rope_theta = float(rope_theta)
+    p.status_flags = int(status_flags) or None
     return p
 
 
 def append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side=None, *, rope="neox", rope_theta=1e4,
-           pos_host=None, stream=None):
+           pos_host=None, stream=None, num_blocks=None, status=None):
     """Enqueue draft_attn_append: write k_new / v_new ([B, n_new, Hkv, d] bf16) at positions
-    pos[b] + i (pos: int32 [B] on the device; pos_host: the same values as a list)."""
+    pos[b] + i (pos: int32 [B] on the device; pos_host: the same values as a list).
+    num_blocks: blocks of the pools the table may name (default: all of them); status: an
+    optional int32 [1] device tensor that receives STATUS_APPEND_BAD_BLOCK."""
     import torch
 
     B, n_new, Hkv, d = k_new.shape
     _check_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side)
     if pos_host is None:
         pos_host = [int(x) for x in pos.cpu().tolist()]
-    p = make_append_params(num_seqs=B, num_new=n_new, num_kv_heads=Hkv, head_dim=d, num_blocks=k_cache.shape[0],
-                           max_blocks_per_seq=block_table.shape[1], rope=rope, rope_theta=rope_theta)
+    status_ptr = 0
+    if status is not None:
+        _expect(status, "status", torch.int32, (1,), k_new.device)
+        status_ptr = status.data_ptr()
+    nb = k_cache.shape[0] if num_blocks is None else int(num_blocks)
+    if nb > k_cache.shape[0]:
+        raise ValueError(f"num_blocks {nb} exceeds the pools' {k_cache.shape[0]} blocks")
+    p = make_append_params(num_seqs=B, num_new=n_new, num_kv_heads=Hkv, head_dim=d, num_blocks=nb,
+                           max_blocks_per_seq=block_table.shape[1], rope=rope, rope_theta=rope_theta,
+                           status_flags=status_ptr)
     s = torch.cuda.current_stream(k_new.device).cuda_stream if stream is None else int(stream)
     st = lib.draft_attn_append(ctypes.byref(p), k_new.data_ptr(), v_new.data_ptr(), block_table.data_ptr(),
                                pos.data_ptr(), _host_i32(pos_host), k_cache.data_ptr(), v_cache.data_ptr(),

@@ -28,6 +28,7 @@ struct AppendArgs {
   __bf16* k;            // [blocks][Hkv][D/8][16][8]
   __bf16* v;            // [blocks][Hkv][D][16]
   __bf16* ks;           // like k, or null
+  uint32_t* status;     // optional device status word, or null
   int32_t B, n_new, Hkv, max_blocks, num_blocks, rope;
   int32_t span;         // logical blocks one sequence's append can touch
   double omega[64];     // rope_theta^(-2i/D)
@@ -102,7 +103,10 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   const int64_t hi64 = (int64_t)p0 + a.n_new < (int64_t)j * 16 + 16 ? (int64_t)p0 + a.n_new : (int64_t)j * 16 + 16;
   if (lo64 >= hi64 || j >= a.max_blocks) return;
   const int32_t id = a.table[(int64_t)b * a.max_blocks + j];
-  if (id < 0 || id >= a.num_blocks) return;  // no block allocated: nothing is written
+  if (id < 0 || id >= a.num_blocks) {  // no block allocated: nothing is written, and it is reported
+    if (tid == 0 && a.status != nullptr) atomicOr(a.status, (uint32_t)DRAFT_ATTN_STATUS_APPEND_BAD_BLOCK);
+    return;
+  }
   const int s0 = (int)(lo64 - (int64_t)j * 16), s1 = (int)(hi64 - (int64_t)j * 16);
   const int32_t i0 = (int32_t)(lo64 - p0);  // index of slot s0's token among the new ones
 
@@ -226,7 +230,7 @@ extern "C" int draft_attn_append(const draft_attn_append_params* p, const void* 
   if (!k_new || !v_new || !block_table || !pos_dev || !k_cache || !v_cache) return DRAFT_ATTN_EINVAL;
   auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
   if (mis(k_new, 16) || mis(v_new, 16) || mis(k_cache, 16) || mis(v_cache, 16) || (k_side && mis(k_side, 16)) ||
-      mis(block_table, 4) || mis(pos_dev, 4))
+      mis(block_table, 4) || mis(pos_dev, 4) || mis(p->status_flags, 4))
     return DRAFT_ATTN_EINVAL;
   AppendArgs a;
   a.k_new = (const __bf16*)k_new;
@@ -236,6 +240,7 @@ extern "C" int draft_attn_append(const draft_attn_append_params* p, const void* 
   a.k = (__bf16*)k_cache;
   a.v = (__bf16*)v_cache;
   a.ks = (__bf16*)k_side;
+  a.status = p->status_flags;
   a.B = p->num_seqs;
   a.n_new = p->num_new;
   a.Hkv = p->num_kv_heads;

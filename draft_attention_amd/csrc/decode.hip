@@ -86,6 +86,7 @@ struct Pass1Args {
   float* dpart;      // fused call: draft parts, out_d [B*T*Hq][D] then lse_d [B*T*Hq]
   void* out;         // [B][T][Hq][D] fp32 or bf16 (single launch)
   float* lse;        // [B][T][Hq] (single launch)
+  uint32_t* status;  // optional device status word (DRAFT_ATTN_STATUS_* bits), or null
   int32_t B, T, Hq, Hkv, G, R, rows_pad, max_blocks, num_blocks;
   int32_t mode, W, S, n0, C, rope, total_items;
   int32_t out_bf16, fold_variant;
@@ -717,7 +718,8 @@ void pass1_kernel(const Pass1Args a) {
                                      : locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si);
   if (!found) {
     // Only when ctx_len on the device disagrees with the host mirror: leave a
-    // neutral record so the merge stays defined.
+    // neutral record so the merge stays defined, and report it.
+    if (tid == 0 && a.status != nullptr) atomicOr(a.status, (uint32_t)DRAFT_ATTN_STATUS_LENGTHS);
     if (tid < a.R) a.stat[(size_t)w * rp + tid] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
     for (int32_t i = tid; i < a.R * D; i += 256) a.acc[(size_t)w * rp * D + i] = 0.f;
     return;
@@ -760,11 +762,14 @@ void pass1_kernel(const Pass1Args a) {
   // of a range's last step may lie past the range and reads as absent. Each
   // thread issues up to eight table loads before it waits for any (a loop of
   // load-then-store waits one round trip per id). A slot with no id loads
-  // entry 0 of the row, which exists, and drops it.
+  // entry 0 of the row, which exists, and drops it. Every block staged here
+  // holds at least one key of the range, so an id outside [0, num_blocks) is a
+  // bad table entry: its keys are masked, and the status word reports it.
   const int32_t nblk = 2 * it.steps;
   const int32_t last_blk = (it.e - 1) >> 4;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
   constexpr int kStageUnroll = 8;
+  bool bad_id = false;
   for (int32_t j0 = 0; j0 < nblk; j0 += 256 * kStageUnroll) {
     int32_t ids[kStageUnroll];
 #pragma unroll
@@ -773,7 +778,9 @@ void pass1_kernel(const Pass1Args a) {
       const int32_t blk = (item_step_key(it, j >> 1) >> 4) + (j & 1);
       const bool ok = j < nblk && blk <= last_blk && blk < a.max_blocks;
       const int32_t id = trow[ok ? blk : 0];
-      ids[u] = ok && id >= 0 && id < a.num_blocks ? id : -1;
+      const bool valid = id >= 0 && id < a.num_blocks;
+      bad_id |= ok && !valid;
+      ids[u] = ok && valid ? id : -1;
     }
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
@@ -781,6 +788,7 @@ void pass1_kernel(const Pass1Args a) {
       if (j < nblk) sbid[j] = ids[u];
     }
   }
+  if (bad_id && a.status != nullptr) atomicOr(a.status, (uint32_t)DRAFT_ATTN_STATUS_BAD_BLOCK);
   __syncthreads();
 
   WaveState<D, RT> st;
@@ -1206,7 +1214,8 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   if ((p->mode == kFold) != (k_side != nullptr)) return DRAFT_ATTN_EINVAL;
   auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
   if (mis(q, 16) || mis(k_cache, 16) || mis(v_cache, 16) || (k_side && mis(k_side, 16)) ||
-      mis(out, 8) || mis(lse, 4) || mis(block_table, 4) || mis(ctx_len_dev, 4) || mis(workspace, 256))
+      mis(out, 8) || mis(lse, 4) || mis(block_table, 4) || mis(ctx_len_dev, 4) || mis(workspace, 256) ||
+      mis(p->status_flags, 4))
     return DRAFT_ATTN_EINVAL;
   if (workspace_bytes < pr.workspace_bytes) return DRAFT_ATTN_ENOSPC;
   log_plan(p, pr);
@@ -1231,6 +1240,7 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   a1.dpart = (float*)(ws + pr.draft_offset);
   a1.out = out;
   a1.lse = lse;
+  a1.status = p->status_flags;
   a1.out_bf16 = p->out_dtype == DRAFT_ATTN_OUT_BF16;
   a1.fold_variant = p->fold_variant;
   a1.beta = p->beta;
@@ -1305,9 +1315,6 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   a2.kappa = p->kappa;
   a2.scale = p->softmax_scale;
 
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();  // clear a stale error so the check below reports ours
-  if (p->prof_events[0]) (void)hipEventRecord((hipEvent_t)p->prof_events[0], s);
   // Every (sequence, kv head) has at least one item, so the single kernel
   // writes every output row.
   const bool single = pr.single && pr.total_items > 0;
@@ -1316,7 +1323,10 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   const bool draft_in_pass1 = fused && p->num_draft_tokens <= 8;
   const int64_t draft_wgs =
       draft_in_pass1 ? ((int64_t)p->num_seqs * p->num_draft_tokens * p->num_q_heads + kWaves - 1) / kWaves : 0;
-  if (pr.total_items + draft_wgs > 0x7fffffff) return DRAFT_ATTN_EINVAL;
+  if (pr.total_items + draft_wgs > 0x7fffffff) return DRAFT_ATTN_EINVAL;  // before anything is enqueued
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a stale error so the check below reports ours
+  if (p->prof_events[0]) (void)hipEventRecord((hipEvent_t)p->prof_events[0], s);
   if (pr.total_items + draft_wgs > 0) {
     const size_t lds = pass1_lds_bytes(pr.chunk, pr.rows_pad, D);
     const bool fold = p->mode == kFold;

@@ -21,6 +21,8 @@
 
 namespace da {
 
+constexpr int kLenArgs = 32;
+
 struct MergeArgs {
   const __bf16* q;   // [B][T][Hq][D]
   const __bf16* kd;  // [B][T][Hkv][D], rotated at the draft positions
@@ -30,6 +32,11 @@ struct MergeArgs {
   float* lse;        // [B][T][Hq], in place
   int32_t B, T, Hq, Hkv, G, mode, W, S, n0;
   float kappa, scale;
+  // Lengths of a batch of up to kLenArgs sequences, from ctx_len_host, as
+  // draft_attn_decode passes them: both calls then take the query scale's n
+  // from the same source (larger batches read ctx_len in device memory).
+  int32_t nlen;            // B when B <= kLenArgs, else 0
+  int32_t len[kLenArgs];
 };
 
 // One wave per (sequence, draft token, query head); lane l owns channels
@@ -55,7 +62,8 @@ __global__ __launch_bounds__(64) void merge_draft_kernel(const MergeArgs a) {
 #pragma unroll
   for (int e = 0; e < CPL; ++e) oc[e] = a.out[qrow * D + lane * CPL + e];
   const float lse_c = a.lse[qrow];
-  const float c = draft_logit_scale(a.scale, a.kappa, visible_count(a.ctx_len[b], a.mode, a.W, a.S), a.n0);
+  const int32_t L = a.nlen > 0 ? a.len[b] : a.ctx_len[b];
+  const float c = draft_logit_scale(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
   float lse_d, od[CPL];
   draft_row_part(dr, t, c, lse_d, od);
   const DraftMerge mg = draft_merge(lse_c, lse_d);
@@ -100,6 +108,8 @@ extern "C" int draft_attn_merge_draft(const draft_attn_params* p, const void* q,
   a.n0 = p->n0;
   a.kappa = p->kappa;
   a.scale = p->softmax_scale;
+  a.nlen = p->num_seqs <= kLenArgs ? p->num_seqs : 0;
+  for (int32_t b = 0; b < kLenArgs; ++b) a.len[b] = b < a.nlen ? ctx_len_host[b] : 0;
   if ((int64_t)a.B * a.T * a.Hq > 0x7fffffff) return DRAFT_ATTN_EINVAL;
   const uint32_t grid = (uint32_t)((int64_t)a.B * a.T * a.Hq);
   hipStream_t s = (hipStream_t)stream;

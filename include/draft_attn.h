@@ -83,15 +83,20 @@
  *   block_table  int32 [B][max_blocks_per_seq]: key j of sequence b lives in
  *                block block_table[b][j / 16], slot j % 16 [WMTP, Builds on:
  *                PagedAttention]. Entries for blocks the mode never reads are
- *                not read and may hold anything (e.g. -1); an entry that is read
- *                and lies outside [0, num_blocks) is treated as a block of
- *                masked keys (never dereferenced).
+ *                not read and may hold anything (e.g. -1). An entry that is read
+ *                (its block holds a key of the visible set) and lies outside
+ *                [0, num_blocks) is treated as a block of masked keys (never
+ *                dereferenced), and sets DRAFT_ATTN_STATUS_BAD_BLOCK in
+ *                *status_flags when that pointer is set.
  *   ctx_len_dev  int32 [B] on the device, the same values as ctx_len_host;
  *                the kernels read it when B > 32 (smaller batches receive the
  *                host values with the launch arguments);
  *   ctx_len_host int32 [B] on the host, read for validation, grid and
  *                workspace sizing. A mismatch gives wrong results but no
- *                out-of-bounds access.
+ *                out-of-bounds access (and sets DRAFT_ATTN_STATUS_LENGTHS when
+ *                a kernel notices it). Because grids are sized from the host
+ *                lengths, a call captured in a HIP graph is bound to the host
+ *                lengths of the capture: re-capture when they change.
  *   out          [B][T][Hq][d], written: fp32 (8-byte aligned) or, with
  *                out_dtype DRAFT_ATTN_OUT_BF16, bf16 rounded to nearest even
  *                from the fp32 result (8-byte aligned).
@@ -112,6 +117,12 @@
  * non-zero return means nothing was enqueued. DRAFT_ATTN_EHIP reports a launch
  * failure seen by hipGetLastError() after enqueueing.
  *
+ * Device-side status: the host cannot see the contents of device tables. When
+ * params.status_flags points to a device uint32, the kernels OR the
+ * DRAFT_ATTN_STATUS_* bits below into it when they meet such a problem (a bad
+ * block id, lengths that disagree); the caller clears the word and reads it
+ * after the stream has completed. NULL: nothing is reported (the default).
+ *
  * Debugging: with DRAFT_ATTN_LOG=1 in the environment (read once, at the first
  * call), draft_attn_decode prints each call's plan to stderr: shapes, mode,
  * chunk size, work items and launch shape. Nothing else reads the environment.
@@ -126,7 +137,7 @@
 extern "C" {
 #endif
 
-#define DRAFT_ATTN_ABI_VERSION 3
+#define DRAFT_ATTN_ABI_VERSION 4
 
 /* modes */
 #define DRAFT_ATTN_FULL 0
@@ -159,6 +170,13 @@ extern "C" {
 #define DRAFT_ATTN_ENOSPC (-2)   /* workspace_bytes below draft_attn_workspace_size() */
 #define DRAFT_ATTN_EHIP (-3)     /* the HIP runtime reported a launch error */
 #define DRAFT_ATTN_ENOTSUP (-4)  /* valid, but the library has no kernel for it */
+
+/* bits ORed into *status_flags by the kernels (device-side status above) */
+#define DRAFT_ATTN_STATUS_BAD_BLOCK 1u        /* decode read a table entry outside [0, num_blocks):
+                                                 its keys were masked */
+#define DRAFT_ATTN_STATUS_LENGTHS 2u          /* ctx_len_dev held fewer work items than ctx_len_host */
+#define DRAFT_ATTN_STATUS_APPEND_BAD_BLOCK 4u /* append met a table entry outside [0, num_blocks):
+                                                 those tokens were not written */
 
 /* Kernel support of the library: head_dim 64 or 128, block_size 16, and
  * G * T <= DRAFT_ATTN_MAX_ROWS query rows per (sequence, kv head). */
@@ -203,6 +221,8 @@ typedef struct draft_attn_params {
                                   on two kernels whatever the setting (its rows are
                                   written by the merge kernel) */
   int32_t out_dtype;           /* DRAFT_ATTN_OUT_F32 (default) or _BF16 */
+  uint32_t* status_flags;      /* optional device word: the kernels OR DRAFT_ATTN_STATUS_* bits
+                                  into it (4-byte aligned); NULL: off */
 } draft_attn_params;
 
 /* int32 values per work item written by draft_attn_plan. */
@@ -303,7 +323,8 @@ int draft_attn_decode_draft(const draft_attn_params* p, const void* q, const voi
  * k_new, v_new: bf16 [B][num_new][Hkv][d] device, 16-byte aligned; pos_dev /
  * pos_host: int32 [B] on device / host with the same values; caches as for
  * draft_attn_decode. Every written block must be allocated in block_table; a
- * token whose table entry lies outside [0, num_blocks) is not written. Nothing
+ * token whose table entry lies outside [0, num_blocks) is not written (and
+ * sets DRAFT_ATTN_STATUS_APPEND_BAD_BLOCK in *status_flags when that is set). Nothing
  * outside the new tokens' slots is touched. Validation is host-side and runs
  * before anything is enqueued. */
 typedef struct draft_attn_append_params {
@@ -318,6 +339,8 @@ typedef struct draft_attn_append_params {
   int32_t rope;                /* DRAFT_ATTN_ROPE_NEOX or _NONE */
   int32_t reserved;            /* must be 0 */
   double rope_theta;           /* finite, > 0 with NEOX */
+  uint32_t* status_flags;      /* optional device word: DRAFT_ATTN_STATUS_APPEND_BAD_BLOCK is
+                                  ORed into it for a token not written; NULL: off */
 } draft_attn_append_params;
 
 /* Defaults: block_size 16, NEOX with rope_theta 1e4, struct_size set. */

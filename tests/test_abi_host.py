@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(da().LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert da().lib.draft_attn_version() == 3
+    assert da().lib.draft_attn_version() == da().ABI_VERSION == 4
 
 
 def test_params_layout_matches_the_c_compiler(tmp_path):
@@ -99,6 +99,7 @@ def test_append_positions_pointers_and_alignment():
     p = mk()
     p.reserved = 3
     assert _append_call(p) == -1
+    assert _append_call(mk(status_flags=0x80001)) == -1   # the status word needs 4-byte alignment
     assert _append_call(mk(num_seqs=0), pos=()) == 0
     assert _append_call(mk(rope="none", rope_theta=0.0), pos=(0, 0), k=None) == -1   # theta unused, pointer checked
 
@@ -177,6 +178,8 @@ def test_bad_lengths_pointers_and_alignment():
     assert call(params(), v=0x30004) == -1
     assert call(params(), out=0x70004) == -1
     assert call(params(), ws=0x100010) == -1
+    assert call(params(status_flags=0x90002)) == -1   # the status word needs 4-byte alignment
+    assert call(params(status_flags=0x90004), ws_bytes=0) == -2   # aligned: the checks go on
     # k_side exactly when FOLD
     assert call(params(), ks=0x40000) == -1
     assert call(params(mode="fold", n_sink=0), fold=True, ks=None) == -1

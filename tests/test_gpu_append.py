@@ -85,6 +85,51 @@ def test_append_far_positions_and_unallocated_blocks():
     assert _pools_equal(_np(gk), rk) and _pools_equal(_np(gv), rv) and _pools_equal(_np(gs), rs)
 
 
+def test_append_entries_outside_the_pool_are_skipped_and_reported():
+    # The pools hold two more blocks than the num_blocks passed, all NaN, and
+    # one new token's block entry names one of them: that block's tokens are not
+    # written (the extra blocks stay NaN), the rest are written as the oracle
+    # writes them, and DRAFT_ATTN_STATUS_APPEND_BAD_BLOCK is set.
+    da = _da()
+    dev = torch.device("cuda:0")
+    d, Hkv, n_new = 128, 2, 20
+    lens = [40, 90]
+    x = synth.make_inputs(ctx_lens=[L + n_new for L in lens], T=1, Hq=Hkv, Hkv=Hkv, d=d, seed=33, fold=True)
+    NB = x["k_cache"].shape[0]
+
+    def widen(t):
+        return torch.cat([t, torch.full((2,) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype)])
+
+    kc, vc, ks = (widen(x[k]).to(dev) for k in ("k_cache", "v_cache", "k_side"))
+    before = [_np(t) for t in (kc, vc, ks)]
+    table = x["block_table"].clone()
+    bad_blk = (lens[1] + n_new - 1) // 16          # sequence 1's last touched block
+    table[1, bad_blk] = NB + 1
+    g = torch.Generator().manual_seed(8)
+    kn = torch.randn((2, n_new, Hkv, d), generator=g).to(torch.bfloat16)
+    vn = torch.randn((2, n_new, Hkv, d), generator=g).to(torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    da.append(kn.to(dev), vn.to(dev), table.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev), kc, vc, ks,
+              rope="neox", rope_theta=5e5, pos_host=lens, num_blocks=NB, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == da.STATUS_APPEND_BAD_BLOCK
+    # oracle: sequence 0 whole, sequence 1 without the tokens of the bad block
+    rk, rv, rs = oracle.append(_np(kn)[:1], _np(vn)[:1], table.numpy()[:1], lens[:1], *before, rope="neox",
+                               rope_theta=5e5)
+    keep = [i for i in range(n_new) if (lens[1] + i) // 16 != bad_blk]
+    assert 0 < len(keep) < n_new and keep == list(range(len(keep)))
+    rk, rv, rs = oracle.append(_np(kn)[1:, keep], _np(vn)[1:, keep], table.numpy()[1:], lens[1:], rk, rv, rs,
+                               rope="neox", rope_theta=5e5)
+    assert _pools_equal(_np(kc), rk) and _pools_equal(_np(vc), rv) and _pools_equal(_np(ks), rs)
+    assert np.all(np.isnan(_np(kc)[NB:])) and np.all(np.isnan(_np(vc)[NB:]))
+    # a clean append leaves the word at zero
+    status.zero_()
+    da.append(kn.to(dev), vn.to(dev), x["block_table"].to(dev), torch.tensor(lens, dtype=torch.int32, device=dev),
+              kc, vc, ks, rope="neox", rope_theta=5e5, pos_host=lens, num_blocks=NB, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+
 def test_cache_built_by_appends_then_decoded():
     # Prefill three sequences entirely through the append kernel (chunks of 64 and
     # a ragged tail), check the pools against the oracle's appends, then decode
