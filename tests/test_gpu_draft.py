@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
     dict(mode="fold", window=700, alpha=2.0, beta=-1.0),
     dict(mode="full", kappa=0.2, n0=256),
     dict(mode="fold", window=300, alpha=4.0, beta=0.5, kappa=0.1, n0=64, rope="none"),
-], ids=["full", "window", "fold", "full-kappa", "fold-kappa-nope"])
+    dict(mode="fold", window=700, alpha=2.0, beta=-1.0, fold_variant="A"),
+    dict(mode="fold", window=300, alpha=0.5, beta=1.0, kappa=0.1, n0=64, fold_variant="B'"),
+], ids=["full", "window", "fold", "full-kappa", "fold-kappa-nope", "fold-A", "fold-Bprime-kappa"])
 @pytest.mark.parametrize("d,T,G", [(128, 4, 4), (64, 8, 2), (128, 1, 8), (128, 32, 1)])
 def test_decode_then_merge_draft(kw, d, T, G):
     import draft_attention_amd as da
@@ -33,8 +35,11 @@ def test_decode_then_merge_draft(kw, d, T, G):
     table, ctx = x["block_table"].to(dev), x["ctx_len"].to(dev)
     side = ks if kw["mode"] == "fold" else None
     out, lse = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, **kw)
+    # the merge does not depend on the FOLD reading: each reading's far mass is
+    # already in the cache result's lse
+    mkw = {k: v for k, v in kw.items() if k != "fold_variant"}
     da.merge_draft(q, kd.to(dev), vd.to(dev), ctx, out, lse, num_blocks=kc.shape[0],
-                   max_blocks_per_seq=table.shape[1], num_kv_heads=Hkv, ctx_lens=lens, rope_theta=5e5, **kw)
+                   max_blocks_per_seq=table.shape[1], num_kv_heads=Hkv, ctx_lens=lens, rope_theta=5e5, **mkw)
     torch.cuda.synchronize()
     n = {k: (v.float().numpy() if torch.is_tensor(v) and v.is_floating_point() else v) for k, v in x.items()}
     ref = oracle.decode_with_draft(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), lens, kw["mode"],
@@ -74,7 +79,9 @@ def test_prepared_merge_draft_matches_the_direct_call():
     dict(mode="window", window=500, n_sink=4),
     dict(mode="fold", window=700, alpha=2.0, beta=-1.0),
     dict(mode="fold", window=300, alpha=4.0, beta=0.5, kappa=0.1, n0=64, rope="none"),
-], ids=["full", "window", "fold", "fold-kappa-nope"])
+    dict(mode="fold", window=700, alpha=2.0, beta=-1.0, fold_variant="A"),
+    dict(mode="fold", window=300, alpha=3.0, beta=0.5, fold_variant="B'"),
+], ids=["full", "window", "fold", "fold-kappa-nope", "fold-A", "fold-Bprime"])
 @pytest.mark.parametrize("d,T,G", [(128, 4, 4), (64, 8, 2), (128, 1, 8), (128, 32, 1), (64, 12, 2)])
 def test_fused_decode_draft_equals_the_two_calls(kw, d, T, G):
     # draft_attn_decode_draft applies the draft part inside the decode's merge
@@ -93,8 +100,9 @@ def test_fused_decode_draft_equals_the_two_calls(kw, d, T, G):
     table, ctx = x["block_table"].to(dev), x["ctx_len"].to(dev)
     side = ks if kw["mode"] == "fold" else None
     out, lse = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, launch="two_pass", **kw)
+    mkw = {k: v for k, v in kw.items() if k != "fold_variant"}
     da.merge_draft(q, kd, vd, ctx, out, lse, num_blocks=kc.shape[0], max_blocks_per_seq=table.shape[1],
-                   num_kv_heads=Hkv, ctx_lens=lens, rope_theta=5e5, **kw)
+                   num_kv_heads=Hkv, ctx_lens=lens, rope_theta=5e5, **mkw)
     for launch in ("auto", "single"):
         fo, fl = da.decode(q, kc, vc, table, ctx, k_side=side, ctx_lens=lens, rope_theta=5e5, launch=launch,
                            k_draft=kd, v_draft=vd, **kw)

@@ -43,9 +43,9 @@ def draw(rnd):
     out_dtype = rnd.choice(["f32", "f32", "bf16"])
     needle = rnd.choice([0.0, 0.0, 0.02])
     # drawn last, so the earlier fields of every case stay as they were: about a
-    # quarter of the cases take the fused call with the step's draft keys (the
-    # oracle's draft reference covers FOLD's default reading only)
-    fused = rnd.random() < 0.25 and kw.get("fold_variant", "B") == "B"
+    # quarter of the cases take the fused call with the step's draft keys, under
+    # every FOLD reading
+    fused = rnd.random() < 0.25
     return dict(d=d, Hkv=Hkv, G=G, T=T, lens=lens, kw=kw, split=split, launch=launch, out_dtype=out_dtype,
                 needle=needle, fused=fused)
 
@@ -86,7 +86,7 @@ def test_random_configuration_matches_the_oracle(case):
         ref = oracle.decode(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), c["lens"],
                             k_side=n["k_side"], rope_theta=5e5, **c["kw"])
     else:
-        kw = {k: v for k, v in c["kw"].items() if k not in ("mode", "fold_variant")}
+        kw = {k: v for k, v in c["kw"].items() if k != "mode"}
         ref = oracle.decode_with_draft(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), c["lens"],
                                        c["kw"]["mode"], kd.float().numpy(), vd.float().numpy(), k_side=n["k_side"],
                                        rope_theta=5e5, **kw)

@@ -208,6 +208,32 @@ def test_batch_above_the_argument_table(launch):
     check(x, dict(mode="window", window=300, n_sink=4), label=f"40 seqs, none empty, {launch}", launch=launch)
 
 
+def test_device_lengths_that_disagree_are_reported():
+    # Batches above 32 sequences read ctx_len from device memory. When it holds
+    # fewer work items than the host lengths the call was planned from, the
+    # kernels leave neutral records for the missing items (no access goes out of
+    # bounds) and set DRAFT_ATTN_STATUS_LENGTHS; with matching lengths the word
+    # stays zero.
+    da = _da()
+    dev = torch.device("cuda:0")
+    lens = [300 + 7 * i for i in range(39)] + [20000]
+    x = synth.make_inputs(ctx_lens=lens, T=2, Hq=8, Hkv=2, d=64, seed=52)
+    g = to_dev(x)
+    p = da.make_params(num_seqs=40, num_draft_tokens=2, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                       num_blocks=x["k_cache"].shape[0], max_blocks_per_seq=x["block_table"].shape[1])
+    items, _ = da.plan(p, lens)
+    assert sum(1 for it in items if it[0] == 39) > 2, "the last sequence must span several items"
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _decode(g, dict(mode="full"), status=status)
+    assert int(status.item()) == 0
+    short = g["ctx_len"].clone()
+    short[39] = 16
+    da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], short, ctx_lens=lens, status=status,
+              rope_theta=5e5, mode="full")
+    torch.cuda.synchronize()
+    assert int(status.item()) == da.STATUS_LENGTHS
+
+
 # ----------------------------------------------------------------------------- paging behaviour
 def test_unread_blocks_may_be_invalid():
     # Blocks wholly outside the window are never read: give them -1 table entries.
@@ -223,6 +249,89 @@ def test_unread_blocks_may_be_invalid():
     y = dict(x, block_table=t)
     out, _ = check(y, kw)
     assert np.array_equal(out, base)
+
+
+def _repage(n, table, keep, Hkv, d):
+    """Host pools holding exactly the kept logical keys of each sequence, in
+    order, in fresh blocks: (k_cache, v_cache, k_side, block_table, lengths)."""
+    nblk = [(len(kk) + 15) // 16 for kk in keep]
+    NB, MB = max(sum(nblk), 1), max(max(nblk), 1)
+    k = np.full((NB, Hkv, d // 8, 16, 8), np.nan)
+    ks = np.full((NB, Hkv, d // 8, 16, 8), np.nan)
+    v = np.full((NB, Hkv, d, 16), np.nan)
+    t = np.full((len(keep), MB), -1, dtype=np.int64)
+    nb = 0
+    for b, kk in enumerate(keep):
+        for i, j in enumerate(kk):
+            if i % 16 == 0:
+                t[b, i // 16] = nb
+                nb += 1
+            sb, ss, db, ds = table[b, j // 16], j % 16, t[b, i // 16], i % 16
+            k[db, :, :, ds, :] = n["k_cache"][sb, :, :, ss, :]
+            ks[db, :, :, ds, :] = n["k_side"][sb, :, :, ss, :]
+            v[db, :, :, ds] = n["v_cache"][sb, :, :, ss]
+    return k, v, ks, t, [len(kk) for kk in keep]
+
+
+@pytest.mark.parametrize("launch", ["two_pass", "single"])
+def test_table_entries_outside_the_pool_are_masked_and_reported(launch):
+    # The pools hold three more blocks than the num_blocks passed, all NaN. A
+    # table entry that is read and names one of them, or is -1, must be masked
+    # (a broken mask shows up as NaN, and no access leaves the allocation) and
+    # must set DRAFT_ATTN_STATUS_BAD_BLOCK. Reference: the oracle over a cache
+    # re-paged with exactly the keys that remain (kappa = 0, so the visible
+    # count does not enter; FOLD without rotation, so the shared position does
+    # not either).
+    da = _da()
+    dev = torch.device("cuda:0")
+    lens, Hkv, d = [3000, 700], 2, 128
+    x = synth.make_inputs(ctx_lens=lens, T=4, Hq=8, Hkv=Hkv, d=d, seed=30, fold=True)
+    NB = x["k_cache"].shape[0]
+
+    def widen(t):
+        return torch.cat([t, torch.full((3,) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype)])
+
+    g = to_dev(dict(x, k_cache=widen(x["k_cache"]), v_cache=widen(x["v_cache"]), k_side=widen(x["k_side"])))
+    n = np_inputs(x)
+    cases = [  # (mode arguments, {(sequence, logical block): bad entry})
+        (dict(mode="full"), {(0, 10): NB, (0, 100): NB + 2, (1, 5): -1, (1, 43): NB + 1}),
+        (dict(mode="window", window=1000, n_sink=20), {(0, 1): NB + 1, (0, 150): NB, (1, 3): -1}),
+        (dict(mode="fold", window=512, alpha=2.0, beta=-1.0, rope="none"), {(0, 20): NB, (1, 2): NB + 1}),
+    ]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for kw, bad in cases:
+        # a clean call leaves the word at zero
+        out0, _ = da.decode(g["q"], g["k_cache"], g["v_cache"], g["block_table"], g["ctx_len"],
+                            k_side=g["k_side"] if kw["mode"] == "fold" else None, ctx_lens=lens, num_blocks=NB,
+                            status=status, launch=launch, **kw)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, kw
+        t = x["block_table"].clone()
+        for (b, j), e in bad.items():
+            t[b, j] = e
+        vis = torch.zeros((2, max(lens)), dtype=torch.uint8, device=dev)
+        out, lse = da.decode(g["q"], g["k_cache"], g["v_cache"], t.to(dev), g["ctx_len"],
+                             k_side=g["k_side"] if kw["mode"] == "fold" else None, ctx_lens=lens, num_blocks=NB,
+                             status=status, debug_visit=vis, launch=launch, **kw)
+        torch.cuda.synchronize()
+        assert int(status.item()) == da.STATUS_BAD_BLOCK, (kw, int(status.item()))
+        status.zero_()
+        keep, want = [], expected_visit(lens, max(lens), **kw)
+        for b, L in enumerate(lens):
+            main, far = oracle.index_sets(L, kw["mode"], kw.get("window", 0), kw.get("n_sink", 0))
+            masked = {j for (bb, j) in bad if bb == b}
+            keys = [int(j) for j in np.concatenate([far, main]) if j // 16 not in masked]
+            keep.append(keys)
+            for j in masked:
+                want[b, 16 * j:16 * j + 16] = 0
+        assert np.array_equal(vis.cpu().numpy(), want), f"{kw}: masked keys were scored"
+        k, v, ks, t2, l2 = _repage(n, x["block_table"].numpy(), keep, Hkv, d)
+        if kw["mode"] == "fold":
+            assert all(len(kk) > kw["window"] for kk in keep)   # the local window is unchanged
+            ref = oracle.decode(n["q"], k, v, t2, l2, k_side=ks, **kw)
+        else:
+            ref = oracle.decode(n["q"], k, v, t2, l2, "full")
+        compare(out.cpu().numpy(), lse.cpu().numpy(), ref, f"bad entries {launch} {kw}")
 
 
 def _relabel_blocks(x, perm):
@@ -295,54 +404,80 @@ def test_empty_batch_and_all_empty_sequences():
 
 
 # ----------------------------------------------------------------------------- full-size workloads
-def _sampled(w, kw, pairs, seed=0, theta=None):
-    """Full-size inputs generated on the GPU; the oracle runs on sampled (seq, kv head) pairs."""
+def _full_size_inputs(w, seed=0):
     dev = torch.device("cuda:0")
-    x = synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed, device=dev,
-                          fold=w.fold, needle_frac=w.needle_frac)
+    return synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed, device=dev,
+                             fold=w.fold, needle_frac=w.needle_frac)
+
+
+def _sampled(w, kw, pairs, x=None, seed=0):
+    """Full-size inputs generated on the GPU (or given); the GPU call runs in the
+    launch configuration the bench times, on every sequence and head; the oracle
+    runs in full on the sampled (seq, kv head) pairs."""
+    if x is None:
+        x = _full_size_inputs(w, seed)
     out, lse, vis = run_gpu(x, kw, visit=True, theta=w.rope_theta)
     want = expected_visit(w.ctx_lens, vis.shape[1], **kw)
     assert np.array_equal(vis, want)
     heads = sorted({g for _, g in pairs})
     G = w.Hq // w.Hkv
+    table = x["block_table"].cpu()
     for g in heads:
-        # one kv head at a time: fp32 host copies of just that head's pools
-        sub = dict(q=x["q"][:, :, g * G:(g + 1) * G].float().cpu().numpy(),
-                   k=x["k_cache"][:, g:g + 1].float().cpu().numpy(),
-                   v=x["v_cache"][:, g:g + 1].float().cpu().numpy(),
-                   ks=None if x["k_side"] is None else x["k_side"][:, g:g + 1].float().cpu().numpy())
         bsel = sorted({b for b, gg in pairs if gg == g})
-        ref = oracle.decode(sub["q"], sub["k"], sub["v"], x["block_table"].cpu().numpy(), w.ctx_lens,
-                            k_side=sub["ks"], rope_theta=w.rope_theta, pairs={(b, 0) for b in bsel}, **kw)
+        # fp32 host copies of just this head's blocks that hold visible keys of
+        # the selected sequences, with their table rows renumbered to the copy
+        rows = table[bsel].clone()
+        for i, b in enumerate(bsel):
+            main, far = oracle.index_sets(w.ctx_lens[b], kw["mode"], kw.get("window", 0), kw.get("n_sink", 0))
+            read = np.zeros(rows.shape[1], dtype=bool)
+            read[np.concatenate([main, far]) // 16] = True
+            rows[i, torch.from_numpy(~read)] = -1
+        used = torch.unique(rows[rows >= 0])
+        remap = torch.full((int(table.max()) + 1,), -1, dtype=torch.int64)
+        remap[used.long()] = torch.arange(used.numel())
+        sub_table = np.where(rows.numpy() >= 0, remap[rows.clamp(min=0).long()].numpy(), -1)
+        idx = used.long().to(x["k_cache"].device)
+        sub = dict(q=x["q"][bsel][:, :, g * G:(g + 1) * G].float().cpu().numpy(),
+                   k=x["k_cache"][idx, g:g + 1].float().cpu().numpy(),
+                   v=x["v_cache"][idx, g:g + 1].float().cpu().numpy(),
+                   ks=None if x["k_side"] is None else x["k_side"][idx, g:g + 1].float().cpu().numpy())
+        ref = oracle.decode(sub["q"], sub["k"], sub["v"], sub_table, [w.ctx_lens[b] for b in bsel],
+                            k_side=sub["ks"], rope_theta=w.rope_theta, **kw)
         o = out[:, :, g * G:(g + 1) * G][bsel]
         ls = lse[:, :, g * G:(g + 1) * G][bsel]
-        r = dict(out=ref["out"][bsel], lse=ref["lse"][bsel])
-        compare(o, ls, r, f"{w.name} {kw} kv={g} seqs={bsel}")
+        compare(o, ls, ref, f"{w.name} {kw} kv={g} seqs={bsel}")
         del sub
 
 
 def test_full_size_llama8b_128k():
     w = synth.workloads()["llama8b_128k"]
+    x = _full_size_inputs(w)
     for kw in w.runs:
-        _sampled(w, kw, pairs=[(0, 0), (0, 5)])
+        _sampled(w, kw, pairs=[(0, g) for g in range(w.Hkv)], x=x)
 
 
 def test_full_size_needles_1m():
     w = synth.workloads()["needles_1m"]
+    x = _full_size_inputs(w)
     for kw in w.runs:
-        _sampled(w, kw, pairs=[(0, 3)])
+        _sampled(w, kw, pairs=[(0, g) for g in range(w.Hkv)], x=x)
 
 
 def test_full_size_fold_256k():
+    # every alpha/beta pair of the workload, each on two kv heads; over the six
+    # pairs every kv head is checked
     w = synth.workloads()["fold_256k"]
-    for kw in (w.runs[0], w.runs[3], w.runs[5]):
-        _sampled(w, kw, pairs=[(0, 1)])
+    x = _full_size_inputs(w)
+    for i, kw in enumerate(w.runs):
+        _sampled(w, kw, pairs=[(0, (2 * i) % w.Hkv), (0, (2 * i + 5) % w.Hkv)], x=x)
 
 
 def test_full_size_batch16_ragged():
+    # every sequence of the batch, each on one kv head (two sequences per head)
     w = synth.workloads()["batch16_ragged"]
+    x = _full_size_inputs(w)
     for kw in w.runs:
-        _sampled(w, kw, pairs=[(0, 2), (7, 2), (15, 6)])
+        _sampled(w, kw, pairs=[(b, b % w.Hkv) for b in range(len(w.ctx_lens))], x=x)
 
 
 @pytest.mark.parametrize("launch,fused", [("two_pass", False), ("single", False), ("auto", True)])
