@@ -30,6 +30,7 @@ _LAUNCHES = {"auto": LAUNCH_AUTO, "two_pass": LAUNCH_TWO_PASS, "single": LAUNCH_
 OUT_F32, OUT_BF16 = 0, 1
 _OUT_DTYPES = {"f32": OUT_F32, "bf16": OUT_BF16}
 MAX_GROUP_ITEMS = 64
+NOALLOC_SCRATCH_BYTES = 16 << 20
 STATUS_BAD_BLOCK, STATUS_LENGTHS, STATUS_APPEND_BAD_BLOCK = 1, 2, 4
 
 
@@ -109,6 +110,8 @@ def _load():
     lib.draft_attn_workspace_size.restype = ctypes.c_int
     lib.draft_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, ctypes.c_size_t, vp]
     lib.draft_attn_decode.restype = ctypes.c_int
+    lib.draft_attn_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp]
+    lib.draft_attn_decode_noalloc.restype = ctypes.c_int
     lib.draft_attn_decode_draft.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                             vp]
     lib.draft_attn_decode_draft.restype = ctypes.c_int
@@ -374,6 +377,45 @@ def decode(q, k_cache, v_cache, block_table, ctx_len, *, mode="full", window=0, 
                    split_keys=split_keys, debug_visit=debug_visit, fold_variant=fold_variant, launch=launch,
                    out_dtype=out_dtype, k_draft=k_draft, v_draft=v_draft, status=status, num_blocks=num_blocks)
     return call(prof_events=prof_events)
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, ctx_len, *, out, lse, ctx_lens, mode="full", window=0,
+                   n_sink=0, alpha=1.0, beta=0.0, kappa=0.0, n0=1, softmax_scale=None, rope="neox", rope_theta=1e4,
+                   k_side=None, stream=None, split_keys=0, fold_variant="B", launch="auto", out_dtype="f32",
+                   status=None):
+    """Enqueue draft_attn_decode_noalloc: decode() without a workspace (the library's
+    per-GPU scratch holds the partial records) and without allocating anything here
+    either: out, lse and the host lengths ctx_lens must be given. Calls that overlap
+    in time on one GPU race on that scratch."""
+    import torch
+
+    B, T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    dev = q.device
+    _expect(q, "q", torch.bfloat16, (B, T, Hq, d), dev)
+    _check_cache(k_cache, v_cache, k_side, Hkv, d, dev)
+    _expect(block_table, "block_table", torch.int32, (B, None), dev)
+    _expect(ctx_len, "ctx_len", torch.int32, (B,), dev)
+    if len(ctx_lens) != B:
+        raise ValueError(f"ctx_lens: {len(ctx_lens)} lengths for {B} sequences")
+    status_ptr = 0
+    if status is not None:
+        _expect(status, "status", torch.int32, (1,), dev)
+        status_ptr = status.data_ptr()
+    p = make_params(num_seqs=B, num_draft_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                    num_blocks=k_cache.shape[0], max_blocks_per_seq=block_table.shape[1], mode=mode,
+                    window=window, n_sink=n_sink, alpha=alpha, beta=beta, kappa=kappa, n0=n0,
+                    softmax_scale=softmax_scale, rope=rope, rope_theta=rope_theta, split_keys=split_keys,
+                    fold_variant=fold_variant, launch=launch, out_dtype=out_dtype, status_flags=status_ptr)
+    _expect(out, "out", _out_torch_dtype(p.out_dtype), (B, T, Hq, d), dev)
+    _expect(lse, "lse", torch.float32, (B, T, Hq), dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    st = lib.draft_attn_decode_noalloc(ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       None if k_side is None else k_side.data_ptr(), block_table.data_ptr(),
+                                       ctx_len.data_ptr(), _host_i32(ctx_lens), out.data_ptr(), lse.data_ptr(), s)
+    if st != OK:
+        raise DraftAttnError(st, "draft_attn_decode_noalloc")
+    return out, lse
 
 
 def _check_append(k_new, v_new, block_table, pos, k_cache, v_cache, k_side):

@@ -44,6 +44,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "draft_part.h"
 #include "host.h"
 #include "plan.h"
@@ -1360,6 +1362,54 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
 }
 
 }  // namespace da
+
+namespace da {
+
+// Scratch of the allocation-free entry point: the workspace of one call (done
+// flags, partial records, draft parts), held by the library in each GPU's
+// memory for the life of the process. In host code `scratch` names a host-side
+// stand-in, not device memory: only the address that hipGetSymbolAddress
+// returns for the current device is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[DRAFT_ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+static ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DRAFT_ATTN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return DRAFT_ATTN_ENOTSUP;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess || slot.ptr == nullptr) return DRAFT_ATTN_EHIP;
+  *out = slot.ptr;
+  return DRAFT_ATTN_OK;
+}
+
+}  // namespace da
+
+extern "C" int draft_attn_decode_noalloc(const draft_attn_params* p, const void* q, const void* k_cache,
+                                         const void* v_cache, const void* k_side, const int32_t* block_table,
+                                         const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
+                                         float* lse, void* stream) {
+  da::Prepared pr;
+  const int st = da::prepare(p, ctx_len_host, &pr);
+  if (st != DRAFT_ATTN_OK) return st;
+  if (pr.workspace_bytes > DRAFT_ATTN_NOALLOC_SCRATCH_BYTES) return DRAFT_ATTN_ENOSPC;
+  if (p->num_seqs == 0) return DRAFT_ATTN_OK;
+  void* ws = nullptr;
+  const int sa = da::scratch_address(&ws);
+  if (sa != DRAFT_ATTN_OK) return sa;
+  return da::decode_impl(p, q, k_cache, v_cache, k_side, block_table, ctx_len_dev, ctx_len_host, nullptr, nullptr,
+                         out, lse, ws, DRAFT_ATTN_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
                                  const void* v_cache, const void* k_side, const int32_t* block_table,

@@ -253,6 +253,29 @@ int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_c
                       const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Allocation-free decode, for callers that cannot allocate device memory or be
+ * handed a workspace: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation. The same call and result as
+ * draft_attn_decode (bit for bit), without the workspace arguments: the partial
+ * records live in a scratch array of DRAFT_ATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory, one per GPU, for the life of the process. The
+ * call allocates nothing and frees nothing. Its first call on a device (the
+ * current device, which must own `stream` and every pointer) looks up that
+ * device's copy of the array once.
+ * A call whose draft_attn_workspace_size exceeds the scratch size returns
+ * DRAFT_ATTN_ENOSPC before enqueueing anything. Every call on one GPU uses the
+ * same array: calls that overlap in time on one GPU (on different streams, or
+ * from different threads) race and give wrong results; serialise them. The
+ * array keeps the last call's contents, which no call depends on (each call's
+ * single-launch done flags are left zero, as with a workspace). */
+#define DRAFT_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int draft_attn_decode_noalloc(const draft_attn_params* p, const void* q, const void* k_cache,
+                              const void* v_cache, const void* k_side, const int32_t* block_table,
+                              const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
+                              float* lse, void* stream);
+
 /* Host-only introspection of the work decomposition a call would use: the
  * chunk size in keys (*chunk_keys: the most keys of one work item), the launch
  * shape (*launch: _TWO_PASS or _SINGLE) and the work items in launch order,

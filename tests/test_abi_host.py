@@ -194,6 +194,29 @@ def test_workspace_too_small_and_prof_events():
     assert call(p) == -1
 
 
+def test_noalloc_refuses_a_call_beyond_its_scratch():
+    # 16 sequences of 1M keys at 8 kv heads need more partial records than the
+    # library's scratch holds: refused on the host, before anything is enqueued
+    # (fake, aligned device addresses, as above).
+    lens = [1 << 20] * 16
+    p = da().make_params(num_seqs=16, num_draft_tokens=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         num_blocks=16 << 16, max_blocks_per_seq=1 << 16)
+    assert da().workspace_size(p, lens) > da().NOALLOC_SCRATCH_BYTES
+    host = (ctypes.c_int32 * 16)(*lens)
+    st = da().lib.draft_attn_decode_noalloc(ctypes.byref(p), 0x10000, 0x20000, 0x30000, None, 0x50000, 0x60000,
+                                            host, 0x70000, 0x80000, None)
+    assert st == da().ENOSPC
+    p.num_draft_tokens = 0                               # validation comes first
+    assert da().lib.draft_attn_decode_noalloc(ctypes.byref(p), 0x10000, 0x20000, 0x30000, None, 0x50000,
+                                              0x60000, host, 0x70000, 0x80000, None) == -1
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    assert "#define DRAFT_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert da().NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
 def test_debug_visit_stride_checked():
     p = params(debug_visit=0x9000, debug_visit_stride=100)
     assert call(p) == -1          # L = 300 > stride
