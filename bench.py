@@ -135,16 +135,31 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes": n, "launches": 3}), flush=True)
 
 
-def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False, launch="auto", shuffle=True):
-    """Generate inputs on the GPU, time `steps` decode calls; returns a result dict."""
+def make_workload_inputs(w, seed, fold, shuffle=True):
+    import torch
+
+    import synth
+    return synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed,
+                             device=torch.device("cuda:0"), fold=fold, needle_frac=w.needle_frac, fill="zero",
+                             shuffle=shuffle)
+
+
+def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False, launch="auto", shuffle=True,
+                  want_dist=None, x=None, floor=False):
+    """Time `steps` decode calls on inputs generated on the GPU (or given as x); returns
+    a result dict. want_events: the streaming pass's mean duration from the library's
+    HIP events, in a second loop of the same calls; want_dist: whole-call hot and cold
+    duration distributions (default: as want_events); floor: also time the call's
+    launch shape with empty kernels, one and two of them, in the same eager loop."""
     import torch
 
     import draft_attention_amd as da
-    import synth
 
+    if want_dist is None:
+        want_dist = want_events
     dev = torch.device("cuda:0")
-    x = synth.make_inputs(ctx_lens=w.ctx_lens, T=w.T, Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=seed, device=dev,
-                          fold=kw["mode"] == "fold", needle_frac=w.needle_frac, fill="zero", shuffle=shuffle)
+    if x is None:
+        x = make_workload_inputs(w, seed, kw["mode"] == "fold", shuffle)
     side = x["k_side"] if kw["mode"] == "fold" else None
     out = torch.empty((len(w.ctx_lens), w.T, w.Hq, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((len(w.ctx_lens), w.T, w.Hq), dtype=torch.float32, device=dev)
@@ -186,11 +201,25 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
         for a, b in pairs:
             ev.destroy(a)
             ev.destroy(b)
+    floors = None
+    if floor:
+        # The same eager loop over the call's launch shape with empty kernels.
+        floors = {}
+        for nk in (1, 2):
+            fcall = da.prepare_launch_floor(p, w.ctx_lens, nk)
+            for _ in range(warmup):
+                fcall()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fcall()
+            torch.cuda.synchronize()
+            floors[nk] = (time.perf_counter() - t0) * 1e3 / steps
     # Whole-call durations from torch events on the call's stream: the
     # distribution of hot steps, then cold steps with the 256 MB Infinity Cache
     # flushed by a 512 MiB write before each call.
     dist = cold = None
-    if want_events:
+    if want_dist:
         import statistics
 
         def pct(v, q):
@@ -243,8 +272,30 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
     keys = sum(visible_keys(L, **kw) for L in w.ctx_lens) * w.Hkv
     bytes_ = keys * 4 * w.d
     res = dict(x=x, kw=kw, ms=ms, ms_eager=ms_eager, pass1_ms=pass1, bytes=bytes_, keys=keys // w.Hkv, chunk=chunk,
-               launch=launch_used, dist=dist, cold=cold, torch_ok=bool(torch.isfinite(out).all().item()))
+               launch=launch_used, dist=dist, cold=cold, floors=floors,
+               torch_ok=bool(torch.isfinite(out).all().item()))
     return res
+
+
+def rate_entry(r):
+    """Secondary-line entry of one timed workload: whole-step rate and, when timed,
+    the streaming pass's duration and rate against the 8 TB/s peak."""
+    gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+    e = dict(ms_per_step=round(r["ms"], 5), draft_steps_per_s=round(1e3 / r["ms"], 1), kv_gbs=round(gbs, 1),
+             pct_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 2), launch=r["launch"], split_keys=r["chunk"])
+    if r["pass1_ms"]:
+        p1 = r["bytes"] / (r["pass1_ms"] * 1e-3) / 1e9
+        e.update(pass1_us=round(r["pass1_ms"] * 1e3, 2), pass1_gbs=round(p1, 1),
+                 pass1_frac=round(p1 / HBM_PEAK_GBS, 4))
+    if r["floors"]:
+        f1, f2 = r["floors"][1] * 1e3, r["floors"][2] * 1e3
+        step = r["ms"] * 1e3
+        floor = f2 if r["launch"] == "two_pass" else f1
+        e.update(floor_one_kernel_us=round(f1, 2), floor_two_kernels_us=round(f2, 2),
+                 above_floor_us=round(step - floor, 2),
+                 floor_note="the call's launch shape with empty kernels, same eager loop; above_floor "
+                            "is the step minus the floor of its own kernel count")
+    return e
 
 
 def copy_ceiling():
@@ -457,11 +508,34 @@ def bench_decode_draft(args):
     import synth
 
     case = args.case or "window_128k"
+    res = time_decode_draft(case, args.steps, args.warmup, args.seed)
+    t1, t2, w1, w2 = res["fused_us"], res["two_calls_us"], res["fused_wall_us"], res["two_calls_wall_us"]
+    L, T, W, Hq, Hkv, d = res["L"], res["T"], res["W"], 32, 8, 128
+    line = {"metric": "draft step attention with draft tokens: us per step", "value": round(t1, 2), "unit": "us",
+            "op": "decode_draft", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "us_per_step_fused": round(t1, 2), "us_per_step_two_calls": round(t2, 2),
+            "us_per_step_wall_fused": round(w1, 2), "us_per_step_wall_two_calls": round(w2, 2),
+            "config": {"case": case, "ctx_len": L, "draft_tokens": T, "window": W, "n_sink": 4, "q_heads": Hq,
+                       "kv_heads": Hkv, "head_dim": d},
+            "roofline": None, "cpu_baseline": None,
+            "note": "latency-bound steps: the fused call saves the separate merge launch"}
+    print(json.dumps(line), flush=True)
+
+
+def time_decode_draft(case, steps, warmup, seed):
+    """Window step with the step's draft tokens, as two calls (decode, then merge_draft)
+    and as the fused call; event-timed means and wall times per step, in us."""
+    import torch
+
+    import draft_attention_amd as da
+    import synth
+
     L, T, W = (131072, 4, 2048) if case == "window_128k" else (1 << 20, 8, 4096)
     Hq, Hkv, d = 32, 8, 128
     dev = torch.device("cuda:0")
-    x = synth.make_inputs(ctx_lens=[L], T=T, Hq=Hq, Hkv=Hkv, d=d, seed=args.seed, device=dev, fill="zero")
-    g = torch.Generator(device=dev).manual_seed(args.seed)
+    x = synth.make_inputs(ctx_lens=[L], T=T, Hq=Hq, Hkv=Hkv, d=d, seed=seed, device=dev, fill="zero")
+    g = torch.Generator(device=dev).manual_seed(seed)
     kd = torch.randn((1, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
     vd = torch.randn((1, T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
     kw = dict(mode="window", window=W, n_sink=4, ctx_lens=[L])
@@ -476,18 +550,48 @@ def bench_decode_draft(args):
         dec()
         mrg()
 
-    t2, w2 = _event_mean_us(two_calls, args.steps, args.warmup)
-    t1, w1 = _event_mean_us(fused, args.steps, args.warmup)
-    line = {"metric": "draft step attention with draft tokens: us per step", "value": round(t1, 2), "unit": "us",
-            "op": "decode_draft", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
-            "us_per_step_fused": round(t1, 2), "us_per_step_two_calls": round(t2, 2),
-            "us_per_step_wall_fused": round(w1, 2), "us_per_step_wall_two_calls": round(w2, 2),
-            "config": {"case": case, "ctx_len": L, "draft_tokens": T, "window": W, "n_sink": 4, "q_heads": Hq,
-                       "kv_heads": Hkv, "head_dim": d},
-            "roofline": None, "cpu_baseline": None,
-            "note": "latency-bound steps: the fused call saves the separate merge launch"}
-    print(json.dumps(line), flush=True)
+    t2, w2 = _event_mean_us(two_calls, steps, warmup)
+    t1, w1 = _event_mean_us(fused, steps, warmup)
+    del x
+    return dict(fused_us=t1, two_calls_us=t2, fused_wall_us=w1, two_calls_wall_us=w2, L=L, T=T, W=W)
+
+
+def secondary_rates(wl, args):
+    """The metric's other draft-step rates, each with its streaming pass's duration
+    and fraction of 8 TB/s: FULL at 128K; the windowed steps (window + sinks) at
+    128K and 1M against their launch floor; FOLD at 256K for every alpha/beta pair
+    of that workload; the 16-sequence ragged batch with query scaling, FULL and
+    FOLD; and the window steps with the step's draft tokens (fused and as two
+    calls). Inputs are generated once per workload."""
+    import torch
+
+    out = {}
+    steps, warmup, seed = args.steps, args.warmup, args.seed
+
+    def run(name, kws, label):
+        w = wl[name]
+        x = make_workload_inputs(w, seed, any(k["mode"] == "fold" for k in kws))
+        for kw in kws:
+            r = time_workload(w, kw, steps, warmup, seed, 0, want_events=True, want_dist=False, graph=args.graph,
+                              x=x, floor=kw["mode"] == "window")
+            out[label(w, kw)] = rate_entry(r)
+            del r
+        del x
+        torch.cuda.empty_cache()
+
+    mode_label = lambda w, kw: f"{w.name}/{kw['mode']}"  # noqa: E731
+    run("llama8b_128k", wl["llama8b_128k"].runs, mode_label)
+    run("needles_1m", [wl["needles_1m"].runs[1]], mode_label)
+    run("fold_256k", wl["fold_256k"].runs,
+        lambda w, kw: f"{w.name}/fold alpha={kw['alpha']:g} beta={kw['beta']:g}")
+    run("batch16_ragged", wl["batch16_ragged"].runs,
+        lambda w, kw: f"{w.name}/{kw['mode']} kappa={kw['kappa']:g}")
+    for case in ("window_128k", "window_1m"):
+        d = time_decode_draft(case, steps, warmup, seed)
+        out[f"decode_draft/{case}"] = dict(fused_us=round(d["fused_us"], 2),
+                                           two_calls_us=round(d["two_calls_us"], 2),
+                                           draft_tokens=d["T"], window=d["W"], ctx_len=d["L"])
+    return out
 
 
 def main():
@@ -517,23 +621,13 @@ def main():
     if args.window is not None:
         kw["window"] = args.window
     r = time_workload(w, kw, args.steps, args.warmup, args.seed, args.split_keys, graph=args.graph,
-                      launch=args.launch, shuffle=not args.contiguous_blocks)
+                      launch=args.launch, shuffle=not args.contiguous_blocks, floor=kw["mode"] == "window")
     gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
     p1 = r["bytes"] / (r["pass1_ms"] * 1e-3) / 1e9
     tag = f"{w.name}/{kw['mode']}"
     secondary = {}
     if not args.no_secondary and w.name == "needles_1m":
-        # The metric's other draft-step rates: FULL at 128K, and the windowed
-        # steps (window + sinks) at 128K and 1M.
-        for name, run in (("llama8b_128k", 0), ("llama8b_128k", 1), ("needles_1m", 1)):
-            w2 = wl[name]
-            kw2 = w2.runs[run]
-            r2 = time_workload(w2, kw2, args.steps, args.warmup, args.seed, 0, want_events=False, graph=args.graph)
-            secondary[f"{name}/{kw2['mode']}"] = dict(ms_per_step=round(r2["ms"], 5),
-                                                       draft_steps_per_s=round(1e3 / r2["ms"], 1),
-                                                       kv_gbs=round(r2["bytes"] / (r2["ms"] * 1e-3) / 1e9, 1),
-                                                       launch=r2["launch"])
-            del r2
+        secondary = secondary_rates(wl, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, kw, r["x"], args.cpu_budget_s)
@@ -574,6 +668,7 @@ def main():
         "step_us_cold": r["cold"],
         "copy_ceiling": copy_ceiling() if not args.no_secondary else None,
         "secondary": secondary,
+        "floor": (None if not r["floors"] else rate_entry(r)),
         "cpu_baseline": cpu,
     }
     if not r["torch_ok"]:

@@ -112,6 +112,8 @@ def _load():
     lib.draft_attn_decode.restype = ctypes.c_int
     lib.draft_attn_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp]
     lib.draft_attn_decode_noalloc.restype = ctypes.c_int
+    lib.draft_attn_launch_floor.argtypes = [P, i32p, ctypes.c_int32, vp]
+    lib.draft_attn_launch_floor.restype = ctypes.c_int
     lib.draft_attn_decode_draft.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                             vp]
     lib.draft_attn_decode_draft.restype = ctypes.c_int
@@ -265,6 +267,24 @@ def launch_of(params: Params, ctx_lens) -> str:
     if st != OK:
         raise DraftAttnError(st, "draft_attn_plan")
     return "single" if launch.value == LAUNCH_SINGLE else "two_pass"
+
+
+def prepare_launch_floor(params: Params, ctx_lens, kernels: int, stream=None):
+    """A callable that enqueues draft_attn_launch_floor: the launch shape of the decode
+    call with these params and lengths, with empty kernels (kernels = 1: the streaming
+    pass's grid only; 2: and the merge pass's)."""
+    import torch
+    host = _host_i32(ctx_lens)
+    s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+    fn = lib.draft_attn_launch_floor
+    ref = ctypes.byref(params)
+
+    def call():
+        st = fn(ref, host, int(kernels), s)
+        if st != OK:
+            raise DraftAttnError(st, "draft_attn_launch_floor")
+    call._keep = (params, host)
+    return call
 
 
 class PreparedDecode:

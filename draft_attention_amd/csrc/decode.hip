@@ -1411,6 +1411,30 @@ extern "C" int draft_attn_decode_noalloc(const draft_attn_params* p, const void*
                          out, lse, ws, DRAFT_ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+namespace da {
+// Launch-floor kernel of draft_attn_launch_floor: it does nothing.
+__global__ __launch_bounds__(256) void empty_kernel() {}
+}  // namespace da
+
+extern "C" int draft_attn_launch_floor(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t kernels,
+                                       void* stream) {
+  da::Prepared pr;
+  const int st = da::prepare(p, ctx_len_host, &pr);
+  if (st != DRAFT_ATTN_OK) return st;
+  if (kernels != 1 && kernels != 2) return DRAFT_ATTN_EINVAL;
+  if (p->num_seqs == 0 || pr.total_items == 0) return DRAFT_ATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const size_t lds = da::pass1_lds_bytes(pr.chunk, pr.rows_pad, p->head_dim);
+  da::empty_kernel<<<(uint32_t)pr.total_items, 256, lds, s>>>();
+  if (kernels == 2) {
+    const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
+    da::empty_kernel<<<rows_total, 256, 0, s>>>();
+  }
+  if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
+  return DRAFT_ATTN_OK;
+}
+
 extern "C" int draft_attn_decode(const draft_attn_params* p, const void* q, const void* k_cache,
                                  const void* v_cache, const void* k_side, const int32_t* block_table,
                                  const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,

@@ -276,6 +276,18 @@ int draft_attn_decode_noalloc(const draft_attn_params* p, const void* q, const v
                               const int32_t* ctx_len_dev, const int32_t* ctx_len_host, void* out,
                               float* lse, void* stream);
 
+/* Measurement aid. A window step reads a constant number of keys whatever the
+ * context ["Windowed-MTP: Removing the Full-Context Draft-KV Tax at
+ * Million-Token Context", Abstract: the window bounds the draft's KV working set
+ * to a constant], so its time is mostly fixed cost. This enqueues the launch
+ * shape draft_attn_decode would use for these params and lengths with kernels
+ * that do nothing: with kernels = 1, one kernel with the streaming pass's grid,
+ * workgroup size and LDS; with kernels = 2, that kernel and then one with the
+ * merge pass's grid. The time of such a step is the launch floor under the
+ * decode call. Validation as for draft_attn_decode; kernels must be 1 or 2. */
+int draft_attn_launch_floor(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t kernels,
+                            void* stream);
+
 /* Host-only introspection of the work decomposition a call would use: the
  * chunk size in keys (*chunk_keys: the most keys of one work item), the launch
  * shape (*launch: _TWO_PASS or _SINGLE) and the work items in launch order,

@@ -217,6 +217,15 @@ def test_noalloc_scratch_size_matches_the_header():
     assert da().NOALLOC_SCRATCH_BYTES == 16 << 20
 
 
+def test_launch_floor_validated_before_launch():
+    host = (ctypes.c_int32 * 2)(*LENS)
+    f = da().lib.draft_attn_launch_floor
+    assert f(ctypes.byref(params()), host, 3, None) == -1
+    assert f(ctypes.byref(params()), host, 0, None) == -1
+    assert f(ctypes.byref(params(num_kv_heads=0)), host, 1, None) == -1
+    assert f(ctypes.byref(params(num_seqs=0)), host, 2, None) == 0
+
+
 def test_debug_visit_stride_checked():
     p = params(debug_visit=0x9000, debug_visit_stride=100)
     assert call(p) == -1          # L = 300 > stride
