@@ -69,7 +69,18 @@ struct SeqTable {
   int32_t nseq;                // B when B <= kArgSeqs, else 0
   int32_t len[kArgSeqs];       // context length of each sequence
   int32_t base[kArgSeqs + 1];  // items (over all kv heads) of the sequences before it
+  float c2[kArgSeqs];          // logit scale softmax_scale * s(n) * log2(e) of each sequence
 };
+
+// Logit scale in the log2 domain, softmax_scale * s(n) * log2(e), with
+// s(n) = 1 + kappa ln(max(n, n0) / n0) formed in fp64 ("SharpDraft: Accelerating
+// Long-Context Speculative Decoding with Cardinality-Aware Query Scaling",
+// Abstract). The host forms it for the sequences of a small batch; kernels form
+// it from ctx_len for larger ones.
+__host__ __device__ inline float logit_scale_log2(float scale, float kappa, int32_t n, int32_t n0) {
+  const double sn = 1.0 + (double)kappa * log((double)(n > n0 ? n : n0) / (double)n0);
+  return (float)((double)scale * sn * 1.4426950408889634);
+}
 
 struct Pass1Args {
   const __bf16* q;
@@ -112,6 +123,24 @@ struct Pass2Args {
   float alpha, beta, kappa, scale;
   SeqTable seqs;
 };
+
+// The kernel arguments are read through the scalar cache, and their first
+// reads miss: the prologue's reads, each waiting on the one before, would pay
+// that miss once per cache line. Reading every 64-byte line once at entry,
+// with independent loads and one wait, pays it once.
+// BYTES: the leading part of the arguments the prologue reads (at most 16
+// lines: the loads all issue before the one wait).
+template <int BYTES, typename T>
+__device__ __forceinline__ void touch_args(const T& a) {
+  static_assert(BYTES <= (int)sizeof(T) && BYTES <= 16 * 64, "touched span");
+  constexpr int N = (BYTES + 63) / 64;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(&a);
+  uint32_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = i < N ? p[16 * i] : 0u;
+  asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]), "s"(v[7]),
+               "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]), "s"(v[12]), "s"(v[13]), "s"(v[14]), "s"(v[15]));
+}
 
 // ---------------------------------------------------------------- lane helpers
 // permlane16/32 swaps return the pair {x[l], x[l^16]} (resp. l^32) in the two halves.
@@ -558,7 +587,11 @@ __device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int3
   constexpr int NQ = D / 4;
   constexpr int ROWS = 16 * RT;
   constexpr int NPJ = ROWS * NQ / 256;  // (row, channel quad) pairs per thread
-  constexpr int IB = 16 / NPJ;          // items per round of partial-output loads
+  // Items per round of partial-output loads: each round is one memory round
+  // trip, so a round holds as many as the registers allow (the streaming state
+  // is dead here). At head dim 64 the kernel runs two or three workgroups per
+  // compute unit and has fewer registers to spare.
+  constexpr int IB = (D == 128 ? 48 : 16) / NPJ;
   constexpr int SPT = kGroupItems / 8;
   static_assert(NPJ * 256 == ROWS * NQ, "pairs must tile the workgroup");
   const int tid = threadIdx.x;
@@ -698,6 +731,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(pass1_occup
 void pass1_kernel(const Pass1Args a) {
   constexpr int KS = D / 32, NT = D / 16, OS = D + 4;  // OS: padded LDS row stride (floats)
   extern __shared__ __align__(16) unsigned char smem[];
+  touch_args<(int)offsetof(Pass1Args, omega)>(a);  // the rotation frequencies, last, only FOLD reads
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i16 = lane & 15, g = lane >> 4;
   const int32_t w = blockIdx.x;
   const int32_t rp = a.rows_pad;
@@ -734,9 +768,8 @@ void pass1_kernel(const Pass1Args a) {
   const Item it = item_of(rg, kidx, a.C);
 
   // Logit scale in the log2 domain: softmax_scale * s(n) * log2(e).
-  const int32_t n = visible_count(L, a.mode, a.W, a.S);
-  const double sn = 1.0 + (double)a.kappa * log((double)(n > a.n0 ? n : a.n0) / (double)a.n0);
-  const float c2 = (float)((double)a.scale * sn * 1.4426950408889634);
+  const float c2 = a.seqs.nseq > 0 ? a.seqs.c2[b]
+                                   : logit_scale_log2(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
 
   // Query rows of this kv head (loaded before the block table so both loads are
   // in flight together): row = t * G + (h - kvh * G), zero-padded to 16 * RT.
@@ -900,13 +933,14 @@ void pass1_kernel(const Pass1Args a) {
     else a.stat[rowbase + tid] = make_float4(M, Lsum, L1sum, 0.f);
   }
   if constexpr (SINGLE) {
-    // Mark this item done, then look at the done flags of the whole group; a
-    // workgroup that finds them all set merges the group and clears them. Each
+    // Mark this item done, then look at the done flags of the whole group. Each
     // workgroup's flag store completes before it reads the flags, so of any two
-    // late workgroups the second sees the first's flag: at least one merges.
-    // Rarely two see all flags at once; both merge and write the same result.
-    // Flags hold kDoneFlag or 0 (every call leaves them 0); any other value,
-    // as in a fresh workspace, reads as not done.
+    // late workgroups the second sees the first's flag: the last to arrive, at
+    // least, finds every flag set. Workgroups that finish together often all do;
+    // each of them then exchanges the group's first flag for 0, and only the one
+    // that gets kDoneFlag back merges the group (and clears the other flags).
+    // Flags hold kDoneFlag or 0 (every call leaves them 0); any other value, as
+    // in a fresh workspace, reads as not done.
     __shared__ int s_last;
     const int64_t g0 = (int64_t)si.base + (int64_t)kvh * si.n;  // first item of the group
     const bool mergeable = si.n <= kGroupItems && g0 + si.n <= (int64_t)a.total_items;
@@ -921,9 +955,14 @@ void pass1_kernel(const Pass1Args a) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
         unsigned long long f = kDoneFlag;
         if (lane < si.n) f = __hip_atomic_load(a.flags + g0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = __ballot(f != kDoneFlag) == 0ull;
-        if (last && lane < si.n) __hip_atomic_store(a.flags + g0 + lane, 0ull, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (__ballot(f != kDoneFlag) == 0ull) {
+          unsigned long long prev = 0ull;
+          if (lane == 0)
+            prev = __hip_atomic_exchange(a.flags + g0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last = __shfl(prev == kDoneFlag ? 1 : 0, 0, 64);
+          if (last && lane > 0 && lane < si.n)
+            __hip_atomic_store(a.flags + g0 + lane, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
       if (lane == 0) s_last = last;
     }
@@ -958,6 +997,7 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   __shared__ float s_scale[TILE];
   __shared__ float4 s_part[2][NG][NQ];
   __shared__ float s_red[4][4];
+  touch_args<(int)sizeof(Pass2Args)>(a);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int q4 = tid % NQ, grp = tid / NQ;
   const int32_t idx = blockIdx.x;
@@ -1280,6 +1320,8 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
     for (int32_t b = 0; b < p->num_seqs; ++b) {
       a1.seqs.len[b] = ctx_len_host[b];
       a1.seqs.base[b] = acc;
+      a1.seqs.c2[b] = logit_scale_log2(p->softmax_scale, p->kappa,
+                                       visible_count(ctx_len_host[b], p->mode, p->window, p->n_sink), p->n0);
       acc += seq_items(seq_ranges(ctx_len_host[b], p->mode, p->window, p->n_sink), pr.chunk, nullptr) *
              p->num_kv_heads;
     }
