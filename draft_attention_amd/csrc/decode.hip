@@ -587,11 +587,9 @@ __device__ __forceinline__ void single_merge(const Pass1Args& a, int32_t b, int3
   constexpr int NQ = D / 4;
   constexpr int ROWS = 16 * RT;
   constexpr int NPJ = ROWS * NQ / 256;  // (row, channel quad) pairs per thread
-  // Items per round of partial-output loads: each round is one memory round
-  // trip, so a round holds as many as the registers allow (the streaming state
-  // is dead here). At head dim 64 the kernel runs two or three workgroups per
-  // compute unit and has fewer registers to spare.
-  constexpr int IB = (D == 128 ? 48 : 16) / NPJ;
+  constexpr int IB = 16 / NPJ;          // items per round of partial-output loads
+  // (Rounds three times as large, at head dim 128, measured slower: 128K
+  // window single launch 16.2 -> 17.9 us, the 16-sequence batch +0.4%.)
   constexpr int SPT = kGroupItems / 8;
   static_assert(NPJ * 256 == ROWS * NQ, "pairs must tile the workgroup");
   const int tid = threadIdx.x;
