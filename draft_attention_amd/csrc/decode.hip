@@ -493,11 +493,12 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
   }
 }
 
-// Dynamic LDS of pass 1: block ids of the item, then the merge buffers.
+// Dynamic LDS of pass 1: block ids of the item, then the merge buffers (row
+// maxima and sums of each wave, and the partial outputs of waves 1-3).
 __host__ __device__ inline size_t pass1_sbid_bytes(int32_t C) { return ((size_t)(C / 16 + 2) * 4 + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t pass1_lds_bytes(int32_t C, int32_t rows_pad, int32_t D) {
   return pass1_sbid_bytes(C) + (size_t)kWaves * rows_pad * (sizeof(float) + sizeof(float2)) +
-         (size_t)2 * rows_pad * (D + 4) * sizeof(float);
+         (size_t)(kWaves - 1) * rows_pad * (D + 4) * sizeof(float);
 }
 
 // Record access on the single-launch path. Work items of one group run on
@@ -746,7 +747,7 @@ void pass1_kernel(const Pass1Args a) {
   int32_t* sbid = (int32_t*)smem;
   float* s_m = (float*)(smem + pass1_sbid_bytes(a.C));  // [kWaves][rp] row maxima
   float2* s_l = (float2*)(s_m + kWaves * rp);           // [kWaves][rp] (acc denominator, plain sum)
-  float* s_o = (float*)(s_l + kWaves * rp);              // [2][rp][OS] partial outputs
+  float* s_o = (float*)(s_l + kWaves * rp);              // [kWaves - 1][rp][OS] partial outputs
   SeqInfo si;
   const bool found = a.seqs.nseq > 0 ? locate_item_table(w, a.seqs, a.mode, a.W, a.S, a.C, &si)
                                      : locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si);
@@ -871,64 +872,68 @@ void pass1_kernel(const Pass1Args a) {
     stream_steps<D, RT, false, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
   }
 
-  // ---- merge the waves: common row maxima, rescale, sum through two LDS slots.
-  if (g == 0) {
+  // ---- merge the waves. Waves 1-3 publish their row maxima, sums and
+  // unscaled partial outputs in LDS; after one barrier, wave 0 rescales all
+  // four states to the common row maxima, sums them and writes the item's
+  // record (one (stat, acc) pair per query row) itself.
+  if (wave > 0) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) s_m[wave * rp + 16 * rt + i16] = st.m[rt];
-  }
-  __syncthreads();
-  const bool sharp = far_part && (a.alpha != 1.f);
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = 16 * rt + i16;
-    float M = s_m[row];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, s_m[k * rp + row]);
-    const float d0 = M == -INFINITY ? -INFINITY : st.m[rt] - M;
-    const float f = ex2(d0);
-    const float fa = sharp ? ex2(a.alpha * d0) : f;
-#pragma unroll
-    for (int n2 = 0; n2 < NT; ++n2) st.o[rt][n2] *= fa;
-    if (g == 0) s_l[wave * rp + row] = make_float2(st.l[rt] * fa, st.l1[rt] * f);
-  }
-  if (wave >= 2) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = 16 * rt + i16;
+      if (g == 0) {
+        s_m[wave * rp + row] = st.m[rt];
+        s_l[wave * rp + row] = make_float2(st.l[rt], st.l1[rt]);
+      }
 #pragma unroll
       for (int n2 = 0; n2 < NT; ++n2)
-        *(f32x4*)(s_o + ((wave - 2) * rp + 16 * rt + i16) * OS + 16 * n2 + 4 * g) = st.o[rt][n2];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int n2 = 0; n2 < NT; ++n2) {
-        f32x4* p = (f32x4*)(s_o + (wave * rp + 16 * rt + i16) * OS + 16 * n2 + 4 * g);
-        *p = *p + st.o[rt][n2];
-      }
+        *(f32x4*)(s_o + ((wave - 1) * rp + row) * OS + 16 * n2 + 4 * g) = st.o[rt][n2];
+    }
   }
   __syncthreads();
   const size_t rowbase = (size_t)w * rp;
-  for (int32_t idx = tid; idx < a.R * (D / 4); idx += 256) {
-    const int32_t row = idx / (D / 4), q4 = idx - row * (D / 4);
-    const f32x4 v0 = *(const f32x4*)(s_o + row * OS + 4 * q4);
-    const f32x4 v1 = *(const f32x4*)(s_o + (rp + row) * OS + 4 * q4);
-    const f32x4 v = v0 + v1;
-    float* dst = a.acc + (rowbase + row) * D + 4 * q4;
-    if constexpr (SINGLE) store_dev4(dst, v[0], v[1], v[2], v[3]);
-    else *(f32x4*)dst = v;
-  }
-  if (tid < a.R) {
-    float M = s_m[tid], Lsum = 0.f, L1sum = 0.f;
+  if (wave == 0) {
+    const bool sharp = far_part && (a.alpha != 1.f);
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
-      M = fmaxf(M, s_m[k * rp + tid]);
-      Lsum += s_l[k * rp + tid].x;
-      L1sum += s_l[k * rp + tid].y;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = 16 * rt + i16;
+      float mk[kWaves], fk[kWaves], fak[kWaves];
+      mk[0] = st.m[rt];
+#pragma unroll
+      for (int k = 1; k < kWaves; ++k) mk[k] = s_m[k * rp + row];
+      float M = mk[0];
+#pragma unroll
+      for (int k = 1; k < kWaves; ++k) M = fmaxf(M, mk[k]);
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        const float d0 = M == -INFINITY ? -INFINITY : mk[k] - M;
+        fk[k] = ex2(d0);
+        fak[k] = sharp ? ex2(a.alpha * d0) : fk[k];
+      }
+      float Lsum = st.l[rt] * fak[0], L1sum = st.l1[rt] * fk[0];
+#pragma unroll
+      for (int k = 1; k < kWaves; ++k) {
+        const float2 l = s_l[k * rp + row];
+        Lsum += l.x * fak[k];
+        L1sum += l.y * fk[k];
+      }
+      const bool live = row < a.R;
+#pragma unroll
+      for (int n2 = 0; n2 < NT; ++n2) {
+        f32x4 v = st.o[rt][n2] * fak[0];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k)
+          v += *(const f32x4*)(s_o + ((k - 1) * rp + row) * OS + 16 * n2 + 4 * g) * fak[k];
+        float* dst = a.acc + (rowbase + row) * D + 16 * n2 + 4 * g;
+        if (live) {
+          if constexpr (SINGLE) store_dev4(dst, v[0], v[1], v[2], v[3]);
+          else *(f32x4*)dst = v;
+        }
+      }
+      if (live && g == 0) {
+        if constexpr (SINGLE) store_dev4((float*)&a.stat[rowbase + row], M, Lsum, L1sum, 0.f);
+        else a.stat[rowbase + row] = make_float4(M, Lsum, L1sum, 0.f);
+      }
     }
-    if constexpr (SINGLE) store_dev4((float*)&a.stat[rowbase + tid], M, Lsum, L1sum, 0.f);
-    else a.stat[rowbase + tid] = make_float4(M, Lsum, L1sum, 0.f);
   }
   if constexpr (SINGLE) {
     // Mark this item done, then look at the done flags of the whole group. Each
@@ -1090,7 +1095,19 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
     const bool is_main = i0 + tid < im;
     M = is_main ? st_m : -INFINITY;
     MF = is_main ? -INFINITY : st_m;
-    block_max2(M, MF);
+    // With at most 64 records every statistic sits in wave 0, which reduces
+    // them alone and publishes the results with the scales (one barrier);
+    // otherwise the whole workgroup reduces them.
+    const bool one_wave = n <= 64;
+    if (one_wave) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        M = fmaxf(M, __shfl_xor(M, off, 64));
+        MF = fmaxf(MF, __shfl_xor(MF, off, 64));
+      }
+    } else {
+      block_max2(M, MF);
+    }
     float sc = 0.f;
     Ls = 0.f; ZF = 0.f; ZFa = 0.f;
     if (st_m != -INFINITY) {
@@ -1104,7 +1121,23 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
       }
     }
     if (tid < n) s_scale[tid] = sc;
-    block_sum3(Ls, ZF, ZFa);   // its barriers also publish s_scale
+    if (one_wave) {
+      if (wv == 0) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          Ls += __shfl_xor(Ls, off, 64);
+          ZF += __shfl_xor(ZF, off, 64);
+          ZFa += __shfl_xor(ZFa, off, 64);
+        }
+        if (lane == 0) {
+          s_red[0][0] = M; s_red[0][1] = MF; s_red[0][2] = Ls; s_red[0][3] = ZF; s_red[1][0] = ZFa;
+        }
+      }
+      __syncthreads();  // publishes s_scale and the reduced statistics
+      M = s_red[0][0]; MF = s_red[0][1]; Ls = s_red[0][2]; ZF = s_red[0][3]; ZFa = s_red[1][0];
+    } else {
+      block_sum3(Ls, ZF, ZFa);   // its barriers also publish s_scale
+    }
 #pragma unroll
     for (int k = 0; k < kFastItems; ++k) {
       const int64_t i = grp + (int64_t)k * NG;
