@@ -45,6 +45,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "draft_part.h"
 #include "host.h"
@@ -494,11 +495,11 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 }
 
 // Dynamic LDS of pass 1: block ids of the item, then the merge buffers (row
-// maxima and sums of each wave, and the partial outputs of waves 1-3).
+// maxima, sums and partial outputs of each wave).
 __host__ __device__ inline size_t pass1_sbid_bytes(int32_t C) { return ((size_t)(C / 16 + 2) * 4 + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t pass1_lds_bytes(int32_t C, int32_t rows_pad, int32_t D) {
   return pass1_sbid_bytes(C) + (size_t)kWaves * rows_pad * (sizeof(float) + sizeof(float2)) +
-         (size_t)(kWaves - 1) * rows_pad * (D + 4) * sizeof(float);
+         (size_t)kWaves * rows_pad * (D + 4) * sizeof(float);
 }
 
 // Record access on the single-launch path. Work items of one group run on
@@ -747,7 +748,7 @@ void pass1_kernel(const Pass1Args a) {
   int32_t* sbid = (int32_t*)smem;
   float* s_m = (float*)(smem + pass1_sbid_bytes(a.C));  // [kWaves][rp] row maxima
   float2* s_l = (float2*)(s_m + kWaves * rp);           // [kWaves][rp] (acc denominator, plain sum)
-  float* s_o = (float*)(s_l + kWaves * rp);              // [kWaves - 1][rp][OS] partial outputs
+  float* s_o = (float*)(s_l + kWaves * rp);              // [kWaves][rp][OS] partial outputs
   SeqInfo si;
   const bool found = a.seqs.nseq > 0 ? locate_item_table(w, a.seqs, a.mode, a.W, a.S, a.C, &si)
                                      : locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si);
@@ -872,68 +873,73 @@ void pass1_kernel(const Pass1Args a) {
     stream_steps<D, RT, false, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
   }
 
-  // ---- merge the waves. Waves 1-3 publish their row maxima, sums and
-  // unscaled partial outputs in LDS; after one barrier, wave 0 rescales all
-  // four states to the common row maxima, sums them and writes the item's
-  // record (one (stat, acc) pair per query row) itself.
-  if (wave > 0) {
+  // ---- merge the waves. Wave rt (rt < RT) combines row tile rt: every wave
+  // publishes its row maxima and sums, and the partial outputs of the tiles it
+  // does not combine, in LDS; after one barrier each combining wave rescales
+  // the four states of its tile to the common row maxima, sums them and writes
+  // the tile's records (one (stat, acc) pair per query row) itself.
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = 16 * rt + i16;
-      if (g == 0) {
-        s_m[wave * rp + row] = st.m[rt];
-        s_l[wave * rp + row] = make_float2(st.l[rt], st.l1[rt]);
-      }
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * rt + i16;
+    if (g == 0) {
+      s_m[wave * rp + row] = st.m[rt];
+      s_l[wave * rp + row] = make_float2(st.l[rt], st.l1[rt]);
+    }
+    if (wave != rt) {
 #pragma unroll
-      for (int n2 = 0; n2 < NT; ++n2)
-        *(f32x4*)(s_o + ((wave - 1) * rp + row) * OS + 16 * n2 + 4 * g) = st.o[rt][n2];
+      for (int n2 = 0; n2 < NT; ++n2) *(f32x4*)(s_o + (wave * rp + row) * OS + 16 * n2 + 4 * g) = st.o[rt][n2];
     }
   }
   __syncthreads();
   const size_t rowbase = (size_t)w * rp;
-  if (wave == 0) {
+  // (the tile index must be a compile-time constant: a register array indexed
+  // by the wave number would be moved to scratch memory)
+  auto combine_tile = [&](auto tile) {
+    constexpr int rt = decltype(tile)::value;
     const bool sharp = far_part && (a.alpha != 1.f);
+    const int row = 16 * rt + i16;
+    float mk[kWaves], fk[kWaves], fak[kWaves];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = 16 * rt + i16;
-      float mk[kWaves], fk[kWaves], fak[kWaves];
-      mk[0] = st.m[rt];
+    for (int k = 0; k < kWaves; ++k) mk[k] = s_m[k * rp + row];
+    float M = mk[0];
 #pragma unroll
-      for (int k = 1; k < kWaves; ++k) mk[k] = s_m[k * rp + row];
-      float M = mk[0];
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, mk[k]);
 #pragma unroll
-      for (int k = 1; k < kWaves; ++k) M = fmaxf(M, mk[k]);
+    for (int k = 0; k < kWaves; ++k) {
+      const float d0 = M == -INFINITY ? -INFINITY : mk[k] - M;
+      fk[k] = ex2(d0);
+      fak[k] = sharp ? ex2(a.alpha * d0) : fk[k];
+    }
+    float Lsum = 0.f, L1sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const float2 l = s_l[k * rp + row];
+      Lsum += l.x * fak[k];
+      L1sum += l.y * fk[k];
+    }
+    const bool live = row < a.R;
+#pragma unroll
+    for (int n2 = 0; n2 < NT; ++n2) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < kWaves; ++k) {
-        const float d0 = M == -INFINITY ? -INFINITY : mk[k] - M;
-        fk[k] = ex2(d0);
-        fak[k] = sharp ? ex2(a.alpha * d0) : fk[k];
+        const f32x4 o = k == rt ? st.o[rt][n2] : *(const f32x4*)(s_o + (k * rp + row) * OS + 16 * n2 + 4 * g);
+        v += o * fak[k];
       }
-      float Lsum = st.l[rt] * fak[0], L1sum = st.l1[rt] * fk[0];
-#pragma unroll
-      for (int k = 1; k < kWaves; ++k) {
-        const float2 l = s_l[k * rp + row];
-        Lsum += l.x * fak[k];
-        L1sum += l.y * fk[k];
-      }
-      const bool live = row < a.R;
-#pragma unroll
-      for (int n2 = 0; n2 < NT; ++n2) {
-        f32x4 v = st.o[rt][n2] * fak[0];
-#pragma unroll
-        for (int k = 1; k < kWaves; ++k)
-          v += *(const f32x4*)(s_o + ((k - 1) * rp + row) * OS + 16 * n2 + 4 * g) * fak[k];
-        float* dst = a.acc + (rowbase + row) * D + 16 * n2 + 4 * g;
-        if (live) {
-          if constexpr (SINGLE) store_dev4(dst, v[0], v[1], v[2], v[3]);
-          else *(f32x4*)dst = v;
-        }
-      }
-      if (live && g == 0) {
-        if constexpr (SINGLE) store_dev4((float*)&a.stat[rowbase + row], M, Lsum, L1sum, 0.f);
-        else a.stat[rowbase + row] = make_float4(M, Lsum, L1sum, 0.f);
+      float* dst = a.acc + (rowbase + row) * D + 16 * n2 + 4 * g;
+      if (live) {
+        if constexpr (SINGLE) store_dev4(dst, v[0], v[1], v[2], v[3]);
+        else *(f32x4*)dst = v;
       }
     }
+    if (live && g == 0) {
+      if constexpr (SINGLE) store_dev4((float*)&a.stat[rowbase + row], M, Lsum, L1sum, 0.f);
+      else a.stat[rowbase + row] = make_float4(M, Lsum, L1sum, 0.f);
+    }
+  };
+  if (wave == 0) combine_tile(std::integral_constant<int, 0>{});
+  if constexpr (RT > 1) {
+    if (wave == 1) combine_tile(std::integral_constant<int, 1>{});
   }
   if constexpr (SINGLE) {
     // Mark this item done, then look at the done flags of the whole group. Each
