@@ -120,12 +120,12 @@ int32_t fit_group_chunk(const draft_attn_params* p, const int32_t* lens, int32_t
 // (sequence, kv head) group then merges it alone: it writes a done flag, reads
 // the group's flags and reads every partial record of the group, n items *
 // padded rows * d * 4 bytes, all through the device's coherence point. When
-// the whole step is one round of workgroups, that tail is on the critical path
-// and pays only for small groups (measured on MI355X: up to about 24 KiB of
-// records, e.g. a 256-key window at 16 rows and d = 128). When there are more
+// the whole step is one round of workgroups, that tail is on the critical path,
+// and on MI355X the two-kernel step now wins every such shape measured (4K to
+// 1M contexts, windows of 64 to 4096 keys: by 0.8 to 6 us). When there are more
 // items than resident workgroups, early groups merge while later items still
-// stream, and it paid up to the largest group measured (160 KiB).
-constexpr size_t kAutoSingleGroupBytes = 24 * 1024;
+// stream, and the single launch still pays up to the largest group measured
+// (160 KiB of records: the 16-sequence batch, 0.2-0.4%).
 constexpr size_t kAutoSingleGroupBytesMultiRound = 160 * 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -201,8 +201,7 @@ int prepare(const draft_attn_params* p, const int32_t* ctx_len_host, Prepared* o
     const size_t group_bytes = (size_t)gmax * rows_pad * p->head_dim * sizeof(float);
     const int64_t slots = (int64_t)kComputeUnits * resident_per_cu(p->head_dim, row_tiles);
     const bool multi_round = count_items(p, ctx_len_host, C) > slots;
-    single = gmax <= DRAFT_ATTN_MAX_GROUP_ITEMS &&
-             group_bytes <= (multi_round ? kAutoSingleGroupBytesMultiRound : kAutoSingleGroupBytes);
+    single = multi_round && gmax <= DRAFT_ATTN_MAX_GROUP_ITEMS && group_bytes <= kAutoSingleGroupBytesMultiRound;
   }
   const int64_t items = count_items(p, ctx_len_host, C);
   if (items > 0x7fffffff) return DRAFT_ATTN_EINVAL;

@@ -418,14 +418,14 @@ def test_batch_with_an_empty_sequence_runs_on_two_kernels():
     for launch in ("auto", "single"):
         p = params(launch=launch)
         assert da().launch_of(p, [300, 0]) == "two_pass"
-        assert da().launch_of(p, [300, 17]) == "single"
+    assert da().launch_of(params(launch="single"), [300, 17]) == "single"
 
 
 def test_auto_launch_rule():
-    # Single launch exactly when the largest group's partial records
-    # (items * padded rows * d * 4 bytes) fit in 24 KiB, or in 160 KiB when the
-    # step has more items than resident workgroups (256 compute units times 1
-    # for d = 128, 3 or 2 for d = 64 with one or two row tiles).
+    # Single launch exactly when the step has more items than resident
+    # workgroups (256 compute units times 1 for d = 128, 3 or 2 for d = 64 with
+    # one or two row tiles) and the largest group's partial records (items *
+    # padded rows * d * 4 bytes) fit in 160 KiB.
     rnd = random.Random(3)
     seen = set()
     for _ in range(200):
@@ -441,11 +441,11 @@ def test_auto_launch_rule():
         gmax = max(_group_counts(items).values())
         tiles = (4 * T + 15) // 16
         slots = 256 * (1 if d == 128 else (3 if tiles == 1 else 2))
-        cap = 160 * 1024 if len(items) > slots else 24 * 1024
+        cap = 160 * 1024 if len(items) > slots else -1
         want = "single" if gmax <= da().MAX_GROUP_ITEMS and gmax * 16 * tiles * d * 4 <= cap else "two_pass"
         assert da().launch_of(p, lens) == want, (mode, lens, T, d)
         seen.add((want, len(items) > slots))
-    assert len(seen) == 4, seen
+    assert seen == {("single", True), ("two_pass", True), ("two_pass", False)}, seen
 
 
 def test_merge_draft_refuses_bf16_output():
