@@ -145,7 +145,7 @@ def make_workload_inputs(w, seed, fold, shuffle=True):
 
 
 def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=False, launch="auto", shuffle=True,
-                  want_dist=None, x=None, floor=False):
+                  want_dist=None, x=None, floor=False, min_warm_s=0.0):
     """Time `steps` decode calls on inputs generated on the GPU (or given as x); returns
     a result dict. want_events: the streaming pass's mean duration from the library's
     HIP events, in a second loop of the same calls; want_dist: whole-call hot and cold
@@ -183,6 +183,14 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    if min_warm_s > 0:
+        # further untimed steps until min_warm_s of them have run (the
+        # secondary workloads: steady clocks, whatever ran before them)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min_warm_s:
+            for _ in range(4):
+                step(None)
+            torch.cuda.synchronize()
     # Timed eager steps.
     t0 = time.perf_counter()
     for k in range(steps):
@@ -562,7 +570,8 @@ def secondary_rates(wl, args):
     128K and 1M against their launch floor; FOLD at 256K for every alpha/beta pair
     of that workload; the 16-sequence ragged batch with query scaling, FULL and
     FOLD; and the window steps with the step's draft tokens (fused and as two
-    calls). Inputs are generated once per workload."""
+    calls). Inputs are generated once per workload; each entry warms up with the
+    run's W steps and then for at least 50 ms more before it is timed."""
     import torch
 
     out = {}
@@ -573,7 +582,7 @@ def secondary_rates(wl, args):
         x = make_workload_inputs(w, seed, any(k["mode"] == "fold" for k in kws))
         for kw in kws:
             r = time_workload(w, kw, steps, warmup, seed, 0, want_events=True, want_dist=False, graph=args.graph,
-                              x=x, floor=kw["mode"] == "window")
+                              x=x, floor=kw["mode"] == "window", min_warm_s=0.05)
             out[label(w, kw)] = rate_entry(r)
             del r
         del x
