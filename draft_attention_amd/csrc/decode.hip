@@ -281,7 +281,8 @@ template <int D>
 struct StepRegs {
   bf16x8 k[2][D / 32];  // A operands of the two S^T key tiles, per k-step
   bf16x8 v[D / 16];     // A operands of the O^T channel tiles
-  int32_t id0, id1;     // physical blocks of the step (-1: masked)
+  int32_t id0, id1;     // physical blocks of the step whose values are loaded (-1: masked)
+  int32_t nid0, nid1;   // physical blocks of the step whose keys were loaded last
 };
 
 // Online-softmax state of one wave (log2 domain). l and l1 are lane-partial
@@ -292,7 +293,7 @@ struct WaveState {
   f32x4 o[RT][D / 16];
 };
 
-template <int D, int RT, bool FAR, bool LO>
+template <int D, int RT, bool FAR, bool LO, bool SPLIT>
 __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* sbid, int32_t b, int32_t kvh,
                                              const Item& it, float c2,
                                              const bf16x8 (&qh)[RT][D / 32], const bf16x8 (&ql)[RT][D / 32],
@@ -328,30 +329,45 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 
   // K/V are read once per call: nontemporal loads keep them from displacing
   // anything in the caches.
-  auto issue = [&](int32_t s, StepRegs<D>& r) {
+  // A step's keys and values load separately: in the main loop the keys of a
+  // buffer's next step go in as soon as the Q.K^T products of its current step
+  // have read theirs (issue_k, before that step's softmax), the values once its
+  // P.V is done (issue_v). So 24 to 32 of a wave's 16-byte loads stay in flight
+  // while it computes, with the registers of two steps.
+  auto issue_k = [&](int32_t s, StepRegs<D>& r) {
     // Every lane reads the same two ids; making them wave-uniform lets the
     // block base addresses and the step's mask test live in scalar registers.
-    r.id0 = __builtin_amdgcn_readfirstlane(sbid[2 * s]);
-    r.id1 = __builtin_amdgcn_readfirstlane(sbid[2 * s + 1]);
+    r.nid0 = __builtin_amdgcn_readfirstlane(sbid[2 * s]);
+    r.nid1 = __builtin_amdgcn_readfirstlane(sbid[2 * s + 1]);
     // masked block: read block 0 (in bounds), values discarded
-    const int32_t kid0 = r.id0 < 0 ? 0 : r.id0;
-    const int32_t kid1 = r.id1 < 0 ? 0 : r.id1;
-    int32_t vid = vhi ? r.id1 : r.id0;
-    vid = vid < 0 ? 0 : vid;
+    const int32_t kid0 = r.nid0 < 0 ? 0 : r.nid0;
+    const int32_t kid1 = r.nid1 < 0 ? 0 : r.nid1;
     const size_t krow = (size_t)(g * 16 + kslot) * 8;
     const __bf16* kp0 = kpool + (size_t)((int64_t)kid0 * a.Hkv + kvh) * (D * 16) + krow;
     const __bf16* kp1 = kpool + (size_t)((int64_t)kid1 * a.Hkv + kvh) * (D * 16) + krow;
-    const __bf16* vp = vpool + ((size_t)((int64_t)vid * a.Hkv + kvh) * D + i16) * 16 + 8 * (g & 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       r.k[0][ks] = __builtin_nontemporal_load((const bf16x8*)(kp0 + ks * 512));
       r.k[1][ks] = __builtin_nontemporal_load((const bf16x8*)(kp1 + ks * 512));
     }
+  };
+  auto issue_v = [&](StepRegs<D>& r) {
+    r.id0 = r.nid0;
+    r.id1 = r.nid1;
+    int32_t vid = vhi ? r.id1 : r.id0;
+    vid = vid < 0 ? 0 : vid;
+    const __bf16* vp = vpool + ((size_t)((int64_t)vid * a.Hkv + kvh) * D + i16) * 16 + 8 * (g & 1);
 #pragma unroll
     for (int n = 0; n < NT; ++n) r.v[n] = __builtin_nontemporal_load((const bf16x8*)(vp + n * 256));
   };
+  auto issue = [&](int32_t s, StepRegs<D>& r) {
+    issue_k(s, r);
+    issue_v(r);
+  };
+  auto no_mid = [] {};
 
-  auto compute = [&](int32_t s, StepRegs<D>& r) {
+  // mid() runs once the step's Q.K^T products have read r.k.
+  auto compute = [&](int32_t s, StepRegs<D>& r, auto&& mid) {
     const int32_t key0 = item_step_key(it, s);
     const bool clean = key0 >= ka && key0 + 32 <= ke && r.id0 >= 0 && r.id1 >= 0;
     // key (relative to key0) is scored iff its block is valid and it lies in the range
@@ -386,6 +402,7 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
         }
         sc[t][rt] = c;
       }
+    mid();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float x[8];
@@ -446,42 +463,65 @@ __device__ __forceinline__ void stream_steps(const Pass1Args& a, const int32_t* 
 
   int32_t s = wave;
   if (s < nsteps) {
-    // Loads run one of this wave's steps ahead of the compute (two buffers).
-    // In the loop every compute starts with the other buffer's loads issued
-    // after its own on every path, so the compiler's wait before it covers
-    // only this step's loads. (With the next issue under a condition inside
-    // the loop, the wait had to cover the newest load as well, which left
-    // almost no loads in flight during the wait.) The last one or two steps
-    // run after the loop.
+    // Two buffers, each holding one of this wave's steps. In the FULL and
+    // WINDOW kernels (SPLIT) a buffer's next step loads while its current step
+    // computes: keys after Q.K^T, values after P.V. In each loop body every
+    // load is unconditional, so the compiler's wait before each product covers
+    // only that product's own loads. (With a load under a condition inside the
+    // loop, the wait had to cover the newest loads as well, which left almost
+    // none in flight during it.) The last steps run after the loop.
     StepRegs<D> ra, rb;
     issue(s, ra);
-    if constexpr (!LO) {
+    if constexpr (SPLIT) {
+      if (s + kWaves < nsteps) issue(s + kWaves, rb);
+      while (s + 3 * kWaves < nsteps) {
+        compute(s, ra, [&] { issue_k(s + 2 * kWaves, ra); });
+        issue_v(ra);
+        compute(s + kWaves, rb, [&] { issue_k(s + 3 * kWaves, rb); });
+        issue_v(rb);
+        s += 2 * kWaves;
+      }
+      if (s + 2 * kWaves < nsteps) {
+        compute(s, ra, [&] { issue_k(s + 2 * kWaves, ra); });
+        issue_v(ra);
+        compute(s + kWaves, rb, no_mid);
+        compute(s + 2 * kWaves, ra, no_mid);
+      } else if (s + kWaves < nsteps) {
+        compute(s, ra, no_mid);
+        compute(s + kWaves, rb, no_mid);
+      } else {
+        compute(s, ra, no_mid);
+      }
+    } else if constexpr (!LO) {
+      // (the FOLD kernels: whole-step loads, one step ahead; with the split
+      // loads above their far path and the 16-sequence FOLD batch measured
+      // 0.5-1% slower)
       while (s + 2 * kWaves < nsteps) {
         issue(s + kWaves, rb);
-        compute(s, ra);
+        compute(s, ra, no_mid);
         issue(s + 2 * kWaves, ra);
-        compute(s + kWaves, rb);
+        compute(s + kWaves, rb, no_mid);
         s += 2 * kWaves;
       }
       if (s + kWaves < nsteps) {
         issue(s + kWaves, rb);
-        compute(s, ra);
-        compute(s + kWaves, rb);
+        compute(s, ra, no_mid);
+        compute(s + kWaves, rb, no_mid);
       } else {
-        compute(s, ra);
+        compute(s, ra, no_mid);
       }
     } else {
       // The rotated far query's mid and lo terms take 64 more registers at
-      // two row tiles; the loop above then runs short of registers, so this
+      // two row tiles; the loops above then run short of registers, so this
       // path keeps one compute per buffer and the stricter wait (measured
       // faster here).
       for (;;) {
         if (s + kWaves < nsteps) issue(s + kWaves, rb);
-        compute(s, ra);
+        compute(s, ra, no_mid);
         s += kWaves;
         if (s >= nsteps) break;
         if (s + kWaves < nsteps) issue(s + kWaves, ra);
-        compute(s, rb);
+        compute(s, rb, no_mid);
         s += kWaves;
         if (s >= nsteps) break;
       }
@@ -865,12 +905,12 @@ void pass1_kernel(const Pass1Args a) {
             ql[rt][ks + KS / 2][e] = (__bf16)(y2 - (float)h2 - (float)m2);
           }
         }
-      stream_steps<D, RT, true, true>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
+      stream_steps<D, RT, true, true, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
     } else {
-      stream_steps<D, RT, true, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
+      stream_steps<D, RT, true, false, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
     }
   } else {
-    stream_steps<D, RT, false, false>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
+    stream_steps<D, RT, false, false, !FOLDK>(a, sbid, b, kvh, it, c2, qh, ql, qm, st);
   }
 
   // ---- merge the waves. Wave rt (rt < RT) combines row tile rt: every wave
