@@ -768,48 +768,62 @@ constexpr int pass1_occupancy(int D, int RT) { return D == 64 ? (RT == 1 ? 3 : 2
 
 template <int D, int RT, bool FOLDK, bool SINGLE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(pass1_occupancy(D, RT))))
-void pass1_kernel(const Pass1Args a) {
+void pass1_kernel(const __bf16* __restrict__ q, const int32_t* __restrict__ table, int32_t first_items,
+                  int32_t L_first, int32_t mode_g_t, int32_t W, int32_t S, int32_t C, int32_t Hq,
+                  int32_t max_blocks, int32_t num_blocks, const Pass1Args a) {
   constexpr int KS = D / 32, NT = D / 16, OS = D + 4;  // OS: padded LDS row stride (floats)
   extern __shared__ __align__(16) unsigned char smem[];
-  touch_args<(int)offsetof(Pass1Args, omega)>(a);  // the rotation frequencies, last, only FOLD reads
+  constexpr int kArgBytes = (int)offsetof(Pass1Args, omega);  // the rotation frequencies, last, only FOLD reads
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i16 = lane & 15, g = lane >> 4;
   const int32_t w = blockIdx.x;
-  const int32_t rp = a.rows_pad;
-  if (!SINGLE && a.kd != nullptr && w >= a.total_items) {
-    // Fused call: workgroups past the work items form the draft parts, one
-    // query row per wave (they do not depend on the cache part, so the merge
-    // kernel only loads them).
-    // (The host adds these workgroups only for T <= 8: holding 16 or 32 draft
-    // keys here raised the register demand of the whole kernel into spills.)
-    const int32_t r = (w - a.total_items) * kWaves + wave;
-    if (r < a.B * a.T * a.Hq) draft_part_store<D, 8>(a, r, lane);
-    return;
+  // Leading scalar arguments, which the hardware places in registers before
+  // the kernel starts: the query, the block table, the launch's shape (mode,
+  // G and T packed in one word) and the first sequence's length and item
+  // count over its kv heads (0: no such shortcut). The first sequence's
+  // workgroups find their item, query rows and table row from these alone and
+  // issue those loads before the argument block arrives; the others read it
+  // first.
+  const int32_t mode = mode_g_t & 0xff, G = (mode_g_t >> 8) & 0xff, T = mode_g_t >> 16, R = T * G;
+  const bool first = w < first_items;
+  SeqInfo si;
+  int32_t L = L_first;
+  if (first) {
+    int32_t nm = 0;
+    si.b = 0;
+    si.base = 0;
+    si.n = seq_items(seq_ranges(L_first, mode, W, S), C, &nm);
+    si.n_main = nm;
+  } else {
+    touch_args<kArgBytes>(a);
+    if (!SINGLE && a.kd != nullptr && w >= a.total_items) {
+      // Fused call: workgroups past the work items form the draft parts, one
+      // query row per wave (they do not depend on the cache part, so the merge
+      // kernel only loads them).
+      // (The host adds these workgroups only for T <= 8: holding 16 or 32 draft
+      // keys here raised the register demand of the whole kernel into spills.)
+      const int32_t r = (w - a.total_items) * kWaves + wave;
+      if (r < a.B * a.T * a.Hq) draft_part_store<D, 8>(a, r, lane);
+      return;
+    }
+    const bool found = a.seqs.nseq > 0 ? locate_item_table(w, a.seqs, mode, W, S, C, &si)
+                                       : locate_item(w, a.ctx_len, a.B, a.Hkv, mode, W, S, C, &si);
+    if (!found) {
+      // Only when ctx_len on the device disagrees with the host mirror: leave a
+      // neutral record so the merge stays defined, and report it.
+      const int32_t rp = a.rows_pad;
+      if (tid == 0 && a.status != nullptr) atomicOr(a.status, (uint32_t)DRAFT_ATTN_STATUS_LENGTHS);
+      if (tid < a.R) a.stat[(size_t)w * rp + tid] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+      for (int32_t i = tid; i < a.R * D; i += 256) a.acc[(size_t)w * rp * D + i] = 0.f;
+      return;
+    }
+    L = a.seqs.nseq > 0 ? a.seqs.len[si.b] : a.ctx_len[si.b];
   }
   int32_t* sbid = (int32_t*)smem;
-  float* s_m = (float*)(smem + pass1_sbid_bytes(a.C));  // [kWaves][rp] row maxima
-  float2* s_l = (float2*)(s_m + kWaves * rp);           // [kWaves][rp] (acc denominator, plain sum)
-  float* s_o = (float*)(s_l + kWaves * rp);              // [kWaves][rp][OS] partial outputs
-  SeqInfo si;
-  const bool found = a.seqs.nseq > 0 ? locate_item_table(w, a.seqs, a.mode, a.W, a.S, a.C, &si)
-                                     : locate_item(w, a.ctx_len, a.B, a.Hkv, a.mode, a.W, a.S, a.C, &si);
-  if (!found) {
-    // Only when ctx_len on the device disagrees with the host mirror: leave a
-    // neutral record so the merge stays defined, and report it.
-    if (tid == 0 && a.status != nullptr) atomicOr(a.status, (uint32_t)DRAFT_ATTN_STATUS_LENGTHS);
-    if (tid < a.R) a.stat[(size_t)w * rp + tid] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-    for (int32_t i = tid; i < a.R * D; i += 256) a.acc[(size_t)w * rp * D + i] = 0.f;
-    return;
-  }
   const int32_t b = si.b;
-  const int32_t L = a.seqs.nseq > 0 ? a.seqs.len[b] : a.ctx_len[b];
   const int32_t rel = w - si.base;
   const int32_t kvh = rel / si.n, kidx = rel - kvh * si.n;
-  const Ranges rg = seq_ranges(L, a.mode, a.W, a.S);
-  const Item it = item_of(rg, kidx, a.C);
-
-  // Logit scale in the log2 domain: softmax_scale * s(n) * log2(e).
-  const float c2 = a.seqs.nseq > 0 ? a.seqs.c2[b]
-                                   : logit_scale_log2(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
+  const Ranges rg = seq_ranges(L, mode, W, S);
+  const Item it = item_of(rg, kidx, C);
 
   // Query rows of this kv head (loaded before the block table so both loads are
   // in flight together): row = t * G + (h - kvh * G), zero-padded to 16 * RT.
@@ -817,10 +831,10 @@ void pass1_kernel(const Pass1Args a) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int32_t row = 16 * rt + i16;
-    const bool ok = row < a.R;
-    const int32_t t = ok ? row / a.G : 0;
-    const int32_t head = kvh * a.G + (ok ? row - t * a.G : 0);
-    const __bf16* qp = a.q + ((int64_t)(b * a.T + t) * a.Hq + head) * D + 8 * g;
+    const bool ok = row < R;
+    const int32_t t = ok ? row / G : 0;
+    const int32_t head = kvh * G + (ok ? row - t * G : 0);
+    const __bf16* qp = q + ((int64_t)(b * T + t) * Hq + head) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 z;
@@ -842,7 +856,7 @@ void pass1_kernel(const Pass1Args a) {
   // bad table entry: its keys are masked, and the status word reports it.
   const int32_t nblk = 2 * it.steps;
   const int32_t last_blk = (it.e - 1) >> 4;
-  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  const int32_t* trow = table + (int64_t)b * max_blocks;
   constexpr int kStageUnroll = 8;
   bool bad_id = false;
   for (int32_t j0 = 0; j0 < nblk; j0 += 256 * kStageUnroll) {
@@ -851,20 +865,31 @@ void pass1_kernel(const Pass1Args a) {
     for (int u = 0; u < kStageUnroll; ++u) {
       const int32_t j = j0 + 256 * u + tid;
       const int32_t blk = (item_step_key(it, j >> 1) >> 4) + (j & 1);
-      const bool ok = j < nblk && blk <= last_blk && blk < a.max_blocks;
+      const bool ok = j < nblk && blk <= last_blk && blk < max_blocks;
       const int32_t id = trow[ok ? blk : 0];
-      const bool valid = id >= 0 && id < a.num_blocks;
+      const bool valid = id >= 0 && id < num_blocks;
       bad_id |= ok && !valid;
       ids[u] = ok && valid ? id : -1;
     }
+    // the argument block, read while the first ids and the query are in flight
+    if (first && j0 == 0) touch_args<kArgBytes>(a);
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
       const int32_t j = j0 + 256 * u + tid;
       if (j < nblk) sbid[j] = ids[u];
     }
   }
+  if (first && nblk <= 0) touch_args<kArgBytes>(a);
   if (bad_id && a.status != nullptr) atomicOr(a.status, (uint32_t)DRAFT_ATTN_STATUS_BAD_BLOCK);
   __syncthreads();
+
+  // Logit scale in the log2 domain: softmax_scale * s(n) * log2(e).
+  const float c2 = a.seqs.nseq > 0 ? a.seqs.c2[b]
+                                   : logit_scale_log2(a.scale, a.kappa, visible_count(L, mode, W, S), a.n0);
+  const int32_t rp = a.rows_pad;
+  float* s_m = (float*)(smem + pass1_sbid_bytes(C));  // [kWaves][rp] row maxima
+  float2* s_l = (float2*)(s_m + kWaves * rp);         // [kWaves][rp] (acc denominator, plain sum)
+  float* s_o = (float*)(s_l + kWaves * rp);            // [kWaves][rp][OS] partial outputs
 
   WaveState<D, RT> st;
   const bool far_part = FOLDK && it.part == kPartFar;
@@ -1025,6 +1050,10 @@ void pass1_kernel(const Pass1Args a) {
 // One workgroup of 256 threads per output row (sequence, kv head, query row).
 // It reduces the row's item records to partition maxima and sums, scales and
 // sums the unnormalised partial outputs, then combines FOLD's partitions.
+// The record pointers, the shape and the first sequence's item counts come as
+// leading scalar arguments (placed in registers before the waves start), so
+// the first sequence's rows issue their record loads without waiting for the
+// argument block.
 // Rows with at most NG * kFastItems items (every workload here) take one round
 // of loads: each thread issues its statistics record and its partial outputs
 // (thread (group g, channel quad c) owns items g, g + NG, ...) before using any
@@ -1037,7 +1066,9 @@ constexpr int kFastItems = 8;
 // 32 (more than 8 draft tokens): wave 0 forms it here, its loads issued with
 // the records', after the row's reductions.
 template <int D, int DM>
-__global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
+__global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ stat, const float* __restrict__ acc,
+                                                    int32_t R, int32_t Hkv, int32_t rows_pad, int32_t total_items,
+                                                    int32_t n_first, int32_t nm_first, const Pass2Args a) {
   constexpr bool FUSED = DM != 0;
   constexpr int TM = DM > 1 ? DM : 1;
   constexpr int NQ = D / 4;     // float4 channel quads per row
@@ -1046,43 +1077,54 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   __shared__ float s_scale[TILE];
   __shared__ float4 s_part[2][NG][NQ];
   __shared__ float s_red[4][4];
-  touch_args<(int)sizeof(Pass2Args)>(a);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int q4 = tid % NQ, grp = tid / NQ;
   const int32_t idx = blockIdx.x;
-  const int32_t row = idx % a.R;
-  const int32_t bh = idx / a.R;
-  const int32_t kvh = bh % a.Hkv;
-  const int32_t b = bh / a.Hkv;
-  SeqInfo si;
-  if (a.seqs.nseq > 0) seq_prefix_table(b, a.seqs, a.mode, a.W, a.S, a.C, &si);
-  else seq_prefix(b, a.ctx_len, a.Hkv, a.mode, a.W, a.S, a.C, &si);
+  const int32_t row = idx % R;
+  const int32_t bh = idx / R;
+  const int32_t kvh = bh % Hkv;
+  const int32_t b = bh / Hkv;
+  // The rows of the first sequence find their items from the leading scalar
+  // arguments alone, which the hardware places in registers before the kernel
+  // starts: their record loads go out before the argument block arrives.
+  const bool first = b == 0 && n_first >= 0;
+  SeqInfo si{0, 0, n_first, nm_first};
+  if (!first) {
+    touch_args<(int)sizeof(Pass2Args)>(a);
+    if (a.seqs.nseq > 0) seq_prefix_table(b, a.seqs, a.mode, a.W, a.S, a.C, &si);
+    else seq_prefix(b, a.ctx_len, Hkv, a.mode, a.W, a.S, a.C, &si);
+  }
   int64_t i0 = (int64_t)si.base + (int64_t)kvh * si.n;
   int64_t im = i0 + si.n_main;
   int64_t i1 = i0 + si.n;
-  const int64_t lim = a.total_items;
+  const int64_t lim = total_items;
   i0 = i0 < lim ? i0 : lim;
   im = im < lim ? im : lim;
   i1 = i1 < lim ? i1 : lim;
-  const float alpha = a.alpha;
-  const size_t rp = (size_t)a.rows_pad;
+  const size_t rp = (size_t)rows_pad;
   const int64_t n = i1 - i0;
-  const float* accrow = a.acc + row * (size_t)D + 4 * q4;
-  const int32_t t = row / a.G;
-  const int32_t head = kvh * a.G + (row - t * a.G);
-  const int64_t orow = (int64_t)(b * a.T + t) * a.Hq + head;
-  float od_row = 0.f, lse_d = 0.f;
-  if constexpr (DM == 1) {
-    const int64_t nd = (int64_t)a.B * a.T * a.Hq;
-    od_row = a.dpart[orow * D + (tid < D ? tid : 0)];
-    lse_d = a.dpart[nd * D + orow];
-  }
+  const float* accrow = acc + row * (size_t)D + 4 * q4;
   __shared__ float s_od[DM > 1 ? D : 1];
   __shared__ float s_lsed;
+  // Output row, and the fused call's draft inputs: these need the argument
+  // block, so they are read once the first record loads are out.
+  int32_t t = 0, head = 0;
+  int64_t orow = 0;
+  float od_row = 0.f, lse_d = 0.f;
   DraftRow<D, TM> dr;
-  if constexpr (DM > 1) {
-    if (wv == 0) draft_row_load(dr, a.q, a.kd, a.vd, b, t, head, kvh, a.T, a.Hq, a.Hkv, lane);
-  }
+  auto draft_inputs = [&] {
+    t = row / a.G;
+    head = kvh * a.G + (row - t * a.G);
+    orow = (int64_t)(b * a.T + t) * a.Hq + head;
+    if constexpr (DM == 1) {
+      const int64_t nd = (int64_t)a.B * a.T * a.Hq;
+      od_row = a.dpart[orow * D + (tid < D ? tid : 0)];
+      lse_d = a.dpart[nd * D + orow];
+    }
+    if constexpr (DM > 1) {
+      if (wv == 0) draft_row_load(dr, a.q, a.kd, a.vd, b, t, head, kvh, a.T, a.Hq, Hkv, lane);
+    }
+  };
 
   // block-wide max / sum of per-thread values through the 4 waves
   auto block_max2 = [&](float& x, float& y) {
@@ -1130,11 +1172,14 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
         const int64_t i = grp + (int64_t)k * NG;
         v[k] = *(const float4*)(accrow + (size_t)(i0 + (i < n ? i : nl)) * rp * D);
       }
-      sv = a.stat[(size_t)(i0 + (has_st ? tid : nl)) * rp + row];
+      sv = stat[(size_t)(i0 + (has_st ? tid : nl)) * rp + row];
     } else {
 #pragma unroll
       for (int k = 0; k < kFastItems; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if (first) touch_args<(int)sizeof(Pass2Args)>(a);  // after the record loads are out
+    draft_inputs();
+    const float alpha = a.alpha;
     const float st_m = sv.x + (has_st ? 0.f : -INFINITY);  // record max (log2), -inf if none
     const float st_y = sv.y * (has_st ? 1.f : 0.f);
     const float st_z = sv.z * (has_st ? 1.f : 0.f);
@@ -1201,17 +1246,20 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
     }
   } else {
     // long rows: maxima, sums, then the partial outputs tile by tile
+    if (first) touch_args<(int)sizeof(Pass2Args)>(a);
+    draft_inputs();
+    const float alpha = a.alpha;
     M = -INFINITY;
     MF = -INFINITY;
     for (int64_t i = i0 + tid; i < i1; i += 256) {
-      const float m = a.stat[(size_t)i * rp + row].x;
+      const float m = stat[(size_t)i * rp + row].x;
       if (i < im) M = fmaxf(M, m);
       else MF = fmaxf(MF, m);
     }
     block_max2(M, MF);
     Ls = 0.f; ZF = 0.f; ZFa = 0.f;
     for (int64_t i = i0 + tid; i < i1; i += 256) {
-      const float4 st = a.stat[(size_t)i * rp + row];
+      const float4 st = stat[(size_t)i * rp + row];
       if (st.x == -INFINITY) continue;
       if (i < im) {
         Ls += st.y * exp2f(st.x - M);
@@ -1231,7 +1279,7 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
         const int64_t t1 = hi < t0 + TILE ? hi : t0 + TILE;
         __syncthreads();
         for (int64_t i = t0 + tid; i < t1; i += 256) {
-          const float m = a.stat[(size_t)i * rp + row].x;
+          const float m = stat[(size_t)i * rp + row].x;
           s_scale[i - t0] = m == -INFINITY ? 0.f : exp2f(sh * (m - ref));
         }
         __syncthreads();
@@ -1252,7 +1300,7 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
   s_part[1][grp][q4] = accp[1];
   __syncthreads();
 
-  const RowCombine cb = combine_row(M, MF, Ls, ZF, ZFa, alpha, a.beta, a.fold_variant);
+  const RowCombine cb = combine_row(M, MF, Ls, ZF, ZFa, a.alpha, a.beta, a.fold_variant);
   float lse_out = cb.lse;
   DraftMerge mg{1.f, 0.f, cb.lse};
   if constexpr (DM > 1) {
@@ -1297,13 +1345,20 @@ __global__ __launch_bounds__(256) void pass2_kernel(const Pass2Args a) {
 template <int D, bool SINGLE>
 static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t grid, size_t lds,
                          hipStream_t s) {
+  // the leading scalar arguments (see pass1_kernel)
+  int32_t first_items = 0;
+  if (a.seqs.nseq > 0) first_items = seq_items(seq_ranges(a.seqs.len[0], a.mode, a.W, a.S), a.C, nullptr) * a.Hkv;
+  const int32_t L_first = a.seqs.nseq > 0 ? a.seqs.len[0] : 0;
+  const int32_t mode_g_t = a.mode | (a.G << 8) | (a.T << 16);
+#define P1_HOT a.q, a.table, first_items, L_first, mode_g_t, a.W, a.S, a.C, a.Hq, a.max_blocks, a.num_blocks, a
   if (row_tiles == 1) {
-    if (fold) pass1_kernel<D, 1, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
-    else pass1_kernel<D, 1, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
+    if (fold) pass1_kernel<D, 1, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
+    else pass1_kernel<D, 1, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
   } else {
-    if (fold) pass1_kernel<D, 2, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
-    else pass1_kernel<D, 2, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(a);
+    if (fold) pass1_kernel<D, 2, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
+    else pass1_kernel<D, 2, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
   }
+#undef P1_HOT
 }
 
 }  // namespace da
@@ -1464,17 +1519,23 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
   if (!single) {
     const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
     const int dm = !fused ? 0 : (draft_in_pass1 ? 1 : (a2.T <= 16 ? 16 : 32));
+    // leading scalar arguments: record pointers, shape, and the first
+    // sequence's item counts (from the launch's sequence table; -1 without one)
+    int32_t n_first = -1, nm_first = 0;
+    if (a2.seqs.nseq > 0) n_first = seq_items(seq_ranges(a2.seqs.len[0], a2.mode, a2.W, a2.S), a2.C, &nm_first);
+#define P2_HOT a2.stat, a2.acc, a2.R, a2.Hkv, a2.rows_pad, a2.total_items, n_first, nm_first
     if (D == 64) {
-      if (dm == 0) pass2_kernel<64, 0><<<rows_total, 256, 0, s>>>(a2);
-      else if (dm == 1) pass2_kernel<64, 1><<<rows_total, 256, 0, s>>>(a2);
-      else if (dm == 16) pass2_kernel<64, 16><<<rows_total, 256, 0, s>>>(a2);
-      else pass2_kernel<64, 32><<<rows_total, 256, 0, s>>>(a2);
+      if (dm == 0) pass2_kernel<64, 0><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
+      else if (dm == 1) pass2_kernel<64, 1><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
+      else if (dm == 16) pass2_kernel<64, 16><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
+      else pass2_kernel<64, 32><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
     } else {
-      if (dm == 0) pass2_kernel<128, 0><<<rows_total, 256, 0, s>>>(a2);
-      else if (dm == 1) pass2_kernel<128, 1><<<rows_total, 256, 0, s>>>(a2);
-      else if (dm == 16) pass2_kernel<128, 16><<<rows_total, 256, 0, s>>>(a2);
-      else pass2_kernel<128, 32><<<rows_total, 256, 0, s>>>(a2);
+      if (dm == 0) pass2_kernel<128, 0><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
+      else if (dm == 1) pass2_kernel<128, 1><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
+      else if (dm == 16) pass2_kernel<128, 16><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
+      else pass2_kernel<128, 32><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
     }
+#undef P2_HOT
   }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
