@@ -1054,18 +1054,21 @@ void pass1_kernel(const __bf16* __restrict__ q, const int32_t* __restrict__ tabl
 // leading scalar arguments (placed in registers before the waves start), so
 // the first sequence's rows issue their record loads without waiting for the
 // argument block.
-// Rows with at most NG * kFastItems items (every workload here) take one round
-// of loads: each thread issues its statistics record and its partial outputs
-// (thread (group g, channel quad c) owns items g, g + NG, ...) before using any
-// of them. Longer rows stream the records in tiles.
-constexpr int kFastItems = 8;
+// Rows with at most NG * FI items (every workload here) take one round of
+// loads: each thread issues its statistics record and its partial outputs
+// (thread (group g, channel quad c) owns items g, g + NG, ... : FI of them)
+// before using any of them. FI (1, 2, 4 or 8) is the smallest that covers the
+// launch's largest group, so no thread loads records it has no use for (4
+// instead of 8 per thread took 0.3-0.6 us off the window steps). Longer rows
+// stream the records in tiles.
+constexpr int kMaxFastItems = 8;
 
 // DM != 0: the fused call; the row is written already merged with its draft
 // part (draft keys 0..t of the step, draft_part.h). DM == 1: pass 1's extra
 // workgroups formed the part, and it is loaded with the records. DM == 16 or
 // 32 (more than 8 draft tokens): wave 0 forms it here, its loads issued with
 // the records', after the row's reductions.
-template <int D, int DM>
+template <int D, int DM, int FI>
 __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ stat, const float* __restrict__ acc,
                                                     int32_t R, int32_t Hkv, int32_t rows_pad, int32_t total_items,
                                                     int32_t n_first, int32_t nm_first, const Pass2Args a) {
@@ -1156,26 +1159,32 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
 
   float M, MF, Ls, ZF, ZFa;
   float4 accp[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
-  if (n <= (int64_t)NG * kFastItems) {
+  if (n <= (int64_t)NG * FI) {
     // One round of loads. Each load reads a valid record (its index clamped to
     // the row's last item) and its value always enters the arithmetic: out of
     // range, a statistic gets -inf added and a partial output a zero weight.
     // A value used only under a condition lets the compiler move its load into
     // the branch and wait for it there, which would serialise the round.
-    const bool has_st = tid < n;
+    // With at most 64 records every wave loads all the statistics (lane l:
+    // record l) and reduces them itself, and each thread takes the scales of
+    // its records from the lanes holding them: no barrier before the weighted
+    // sums. Otherwise thread tid holds record tid and the workgroup reduces.
+    const bool one_wave = n <= 64;
+    const int32_t sid = one_wave ? lane : tid;
+    const bool has_st = sid < n;
     const int64_t nl = n > 0 ? n - 1 : 0;  // n == 0: nothing is read
-    float4 v[kFastItems];
+    float4 v[FI];
     float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
     if (n > 0) {
 #pragma unroll
-      for (int k = 0; k < kFastItems; ++k) {
+      for (int k = 0; k < FI; ++k) {
         const int64_t i = grp + (int64_t)k * NG;
         v[k] = *(const float4*)(accrow + (size_t)(i0 + (i < n ? i : nl)) * rp * D);
       }
-      sv = stat[(size_t)(i0 + (has_st ? tid : nl)) * rp + row];
+      sv = stat[(size_t)(i0 + (has_st ? sid : nl)) * rp + row];
     } else {
 #pragma unroll
-      for (int k = 0; k < kFastItems; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < FI; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (first) touch_args<(int)sizeof(Pass2Args)>(a);  // after the record loads are out
     draft_inputs();
@@ -1183,13 +1192,9 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
     const float st_m = sv.x + (has_st ? 0.f : -INFINITY);  // record max (log2), -inf if none
     const float st_y = sv.y * (has_st ? 1.f : 0.f);
     const float st_z = sv.z * (has_st ? 1.f : 0.f);
-    const bool is_main = i0 + tid < im;
+    const bool is_main = i0 + sid < im;
     M = is_main ? st_m : -INFINITY;
     MF = is_main ? -INFINITY : st_m;
-    // With at most 64 records every statistic sits in wave 0, which reduces
-    // them alone and publishes the results with the scales (one barrier);
-    // otherwise the whole workgroup reduces them.
-    const bool one_wave = n <= 64;
     if (one_wave) {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
@@ -1211,29 +1216,23 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
         ZFa = st_y * sc;
       }
     }
-    if (tid < n) s_scale[tid] = sc;
     if (one_wave) {
-      if (wv == 0) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          Ls += __shfl_xor(Ls, off, 64);
-          ZF += __shfl_xor(ZF, off, 64);
-          ZFa += __shfl_xor(ZFa, off, 64);
-        }
-        if (lane == 0) {
-          s_red[0][0] = M; s_red[0][1] = MF; s_red[0][2] = Ls; s_red[0][3] = ZF; s_red[1][0] = ZFa;
-        }
+      for (int off = 32; off >= 1; off >>= 1) {
+        Ls += __shfl_xor(Ls, off, 64);
+        ZF += __shfl_xor(ZF, off, 64);
+        ZFa += __shfl_xor(ZFa, off, 64);
       }
-      __syncthreads();  // publishes s_scale and the reduced statistics
-      M = s_red[0][0]; MF = s_red[0][1]; Ls = s_red[0][2]; ZF = s_red[0][3]; ZFa = s_red[1][0];
     } else {
+      if (tid < n) s_scale[tid] = sc;
       block_sum3(Ls, ZF, ZFa);   // its barriers also publish s_scale
     }
 #pragma unroll
-    for (int k = 0; k < kFastItems; ++k) {
+    for (int k = 0; k < FI; ++k) {
       const int64_t i = grp + (int64_t)k * NG;
       const bool ok = i < n;
-      const float sk = s_scale[ok ? i : 0] * (ok ? 1.f : 0.f);
+      const float s_i = one_wave ? __shfl(sc, ok ? (int)i : 0, 64) : s_scale[ok ? i : 0];
+      const float sk = s_i * (ok ? 1.f : 0.f);
       const float wm = i0 + i < im ? sk : 0.f, wf = i0 + i < im ? 0.f : sk;
       accp[0].x += wm * v[k].x;
       accp[0].y += wm * v[k].y;
@@ -1342,6 +1341,28 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
 }
 
 // ---------------------------------------------------------------- launch
+template <int D, int FI>
+static void launch_pass2_fi(int dm, uint32_t grid, hipStream_t s, const float4* stat, const float* acc, int32_t R,
+                            int32_t Hkv, int32_t rows_pad, int32_t total_items, int32_t n_first, int32_t nm_first,
+                            const Pass2Args& a) {
+#define P2_ARGS stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a
+  if (dm == 0) pass2_kernel<D, 0, FI><<<grid, 256, 0, s>>>(P2_ARGS);
+  else if (dm == 1) pass2_kernel<D, 1, FI><<<grid, 256, 0, s>>>(P2_ARGS);
+  else if (dm == 16) pass2_kernel<D, 16, FI><<<grid, 256, 0, s>>>(P2_ARGS);
+  else pass2_kernel<D, 32, FI><<<grid, 256, 0, s>>>(P2_ARGS);
+#undef P2_ARGS
+}
+
+template <int D>
+static void launch_pass2(int dm, int fi, uint32_t grid, hipStream_t s, const float4* stat, const float* acc,
+                         int32_t R, int32_t Hkv, int32_t rows_pad, int32_t total_items, int32_t n_first,
+                         int32_t nm_first, const Pass2Args& a) {
+  if (fi == 1) launch_pass2_fi<D, 1>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
+  else if (fi == 2) launch_pass2_fi<D, 2>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
+  else if (fi == 4) launch_pass2_fi<D, 4>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
+  else launch_pass2_fi<D, kMaxFastItems>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
+}
+
 template <int D, bool SINGLE>
 static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t grid, size_t lds,
                          hipStream_t s) {
@@ -1524,17 +1545,12 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
     int32_t n_first = -1, nm_first = 0;
     if (a2.seqs.nseq > 0) n_first = seq_items(seq_ranges(a2.seqs.len[0], a2.mode, a2.W, a2.S), a2.C, &nm_first);
 #define P2_HOT a2.stat, a2.acc, a2.R, a2.Hkv, a2.rows_pad, a2.total_items, n_first, nm_first
-    if (D == 64) {
-      if (dm == 0) pass2_kernel<64, 0><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-      else if (dm == 1) pass2_kernel<64, 1><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-      else if (dm == 16) pass2_kernel<64, 16><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-      else pass2_kernel<64, 32><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-    } else {
-      if (dm == 0) pass2_kernel<128, 0><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-      else if (dm == 1) pass2_kernel<128, 1><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-      else if (dm == 16) pass2_kernel<128, 16><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-      else pass2_kernel<128, 32><<<rows_total, 256, 0, s>>>(P2_HOT, a2);
-    }
+    // records each thread of the merge kernel loads in its one round
+    const int32_t ng = 256 / (D / 4);
+    const int32_t fi = pr.max_group_items <= ng ? 1 : pr.max_group_items <= 2 * ng ? 2
+                     : pr.max_group_items <= 4 * ng ? 4 : kMaxFastItems;
+    if (D == 64) launch_pass2<64>(dm, fi, rows_total, s, P2_HOT, a2);
+    else launch_pass2<128>(dm, fi, rows_total, s, P2_HOT, a2);
 #undef P2_HOT
   }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
