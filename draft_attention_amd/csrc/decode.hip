@@ -163,6 +163,35 @@ __device__ __forceinline__ float pair_add32(float x) {
 }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// All-lane reductions of a wave through the lane crossbars that need no LDS:
+// DPP quad permutations and row mirrors within each 16-lane row, then the
+// permlane16/32 swaps across rows. Every step combines a lane with a partner
+// that holds the mirror-image operand pair, so by commutativity every lane
+// ends with the same bits (rotations would leave the lanes of a row with sums
+// associated differently).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppMirror = 0x140;      // row_mirror: lane i <-> 15 - i of its row
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7 - i of its half row
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return pair_max32(pair_max16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppMirror>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return pair_add32(pair_add16(x));
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -1131,11 +1160,8 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
 
   // block-wide max / sum of per-thread values through the 4 waves
   auto block_max2 = [&](float& x, float& y) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      x = fmaxf(x, __shfl_xor(x, off, 64));
-      y = fmaxf(y, __shfl_xor(y, off, 64));
-    }
+    x = wave_max(x);
+    y = wave_max(y);
     if (lane == 0) { s_red[wv][0] = x; s_red[wv][1] = y; }
     __syncthreads();
     x = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
@@ -1143,12 +1169,9 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
     __syncthreads();
   };
   auto block_sum3 = [&](float& x, float& y, float& z) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      x += __shfl_xor(x, off, 64);
-      y += __shfl_xor(y, off, 64);
-      z += __shfl_xor(z, off, 64);
-    }
+    x = wave_sum(x);
+    y = wave_sum(y);
+    z = wave_sum(z);
     if (lane == 0) { s_red[wv][0] = x; s_red[wv][1] = y; s_red[wv][2] = z; }
     __syncthreads();
     x = s_red[0][0] + s_red[1][0] + s_red[2][0] + s_red[3][0];
@@ -1196,11 +1219,8 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
     M = is_main ? st_m : -INFINITY;
     MF = is_main ? -INFINITY : st_m;
     if (one_wave) {
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        M = fmaxf(M, __shfl_xor(M, off, 64));
-        MF = fmaxf(MF, __shfl_xor(MF, off, 64));
-      }
+      M = wave_max(M);
+      MF = wave_max(MF);
     } else {
       block_max2(M, MF);
     }
@@ -1217,12 +1237,9 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
       }
     }
     if (one_wave) {
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        Ls += __shfl_xor(Ls, off, 64);
-        ZF += __shfl_xor(ZF, off, 64);
-        ZFa += __shfl_xor(ZFa, off, 64);
-      }
+      Ls = wave_sum(Ls);
+      ZF = wave_sum(ZF);
+      ZFa = wave_sum(ZFa);
     } else {
       if (tid < n) s_scale[tid] = sc;
       block_sum3(Ls, ZF, ZFa);   // its barriers also publish s_scale
