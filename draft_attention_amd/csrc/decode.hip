@@ -26,8 +26,8 @@
 //                             channel-major value block (one 16-byte load = 8
 //                             consecutive keys of one channel), B = P in bf16.
 // K and V fragments go from HBM to registers with 128-bit nontemporal loads and
-// no LDS staging; the next step's loads are issued before the current step
-// computes. The key permutation inside a step is chosen so that the softmax
+// no LDS staging; each wave holds two steps, and a buffer's next step loads
+// while the current one computes. The key permutation inside a step is chosen so that the softmax
 // output of the Q.K^T product is already the B operand of the P.V product. The
 // four waves' states merge through LDS into one record per item and row.
 // Pass 2 merges the per-item (max, sums, unnormalised output) records with the
@@ -37,7 +37,9 @@
 // performs that merge itself (records and flags travel through device-scope
 // accesses, since the eight XCDs' L2 caches are not coherent with each other).
 // Small batches receive their lengths and item offsets with the launch
-// arguments, so neither kernel starts with a dependent read of ctx_len.
+// arguments, so neither kernel starts with a dependent read of ctx_len, and
+// the first sequence's addressing comes in preloaded scalar arguments, so its
+// workgroups issue their first loads before the argument block arrives.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -127,8 +129,9 @@ struct Pass2Args {
 
 // The kernel arguments are read through the scalar cache, and their first
 // reads miss: the prologue's reads, each waiting on the one before, would pay
-// that miss once per cache line. Reading every 64-byte line once at entry,
-// with independent loads and one wait, pays it once.
+// that miss once per cache line. Reading every 64-byte line once, with
+// independent loads and one wait, pays it once (at entry, or, in workgroups
+// that start from preloaded arguments, once their first loads are out).
 // BYTES: the leading part of the arguments the prologue reads (at most 16
 // lines: the loads all issue before the one wait).
 template <int BYTES, typename T>
