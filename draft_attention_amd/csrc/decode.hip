@@ -1361,26 +1361,34 @@ __global__ __launch_bounds__(256) void pass2_kernel(const float4* __restrict__ s
 }
 
 // ---------------------------------------------------------------- launch
+// The merge kernel's leading scalar arguments (see pass2_kernel), gathered on
+// the host.
+struct Pass2Lead {
+  const float4* stat;
+  const float* acc;
+  int32_t R, Hkv, rows_pad, total_items, n_first, nm_first;
+};
+
+template <int D, int DM, int FI>
+static void launch_pass2_k(uint32_t grid, hipStream_t s, const Pass2Lead& h, const Pass2Args& a) {
+  pass2_kernel<D, DM, FI><<<grid, 256, 0, s>>>(h.stat, h.acc, h.R, h.Hkv, h.rows_pad, h.total_items, h.n_first,
+                                               h.nm_first, a);
+}
+
 template <int D, int FI>
-static void launch_pass2_fi(int dm, uint32_t grid, hipStream_t s, const float4* stat, const float* acc, int32_t R,
-                            int32_t Hkv, int32_t rows_pad, int32_t total_items, int32_t n_first, int32_t nm_first,
-                            const Pass2Args& a) {
-#define P2_ARGS stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a
-  if (dm == 0) pass2_kernel<D, 0, FI><<<grid, 256, 0, s>>>(P2_ARGS);
-  else if (dm == 1) pass2_kernel<D, 1, FI><<<grid, 256, 0, s>>>(P2_ARGS);
-  else if (dm == 16) pass2_kernel<D, 16, FI><<<grid, 256, 0, s>>>(P2_ARGS);
-  else pass2_kernel<D, 32, FI><<<grid, 256, 0, s>>>(P2_ARGS);
-#undef P2_ARGS
+static void launch_pass2_fi(int dm, uint32_t grid, hipStream_t s, const Pass2Lead& h, const Pass2Args& a) {
+  if (dm == 0) launch_pass2_k<D, 0, FI>(grid, s, h, a);
+  else if (dm == 1) launch_pass2_k<D, 1, FI>(grid, s, h, a);
+  else if (dm == 16) launch_pass2_k<D, 16, FI>(grid, s, h, a);
+  else launch_pass2_k<D, 32, FI>(grid, s, h, a);
 }
 
 template <int D>
-static void launch_pass2(int dm, int fi, uint32_t grid, hipStream_t s, const float4* stat, const float* acc,
-                         int32_t R, int32_t Hkv, int32_t rows_pad, int32_t total_items, int32_t n_first,
-                         int32_t nm_first, const Pass2Args& a) {
-  if (fi == 1) launch_pass2_fi<D, 1>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
-  else if (fi == 2) launch_pass2_fi<D, 2>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
-  else if (fi == 4) launch_pass2_fi<D, 4>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
-  else launch_pass2_fi<D, kMaxFastItems>(dm, grid, s, stat, acc, R, Hkv, rows_pad, total_items, n_first, nm_first, a);
+static void launch_pass2(int dm, int fi, uint32_t grid, hipStream_t s, const Pass2Lead& h, const Pass2Args& a) {
+  if (fi == 1) launch_pass2_fi<D, 1>(dm, grid, s, h, a);
+  else if (fi == 2) launch_pass2_fi<D, 2>(dm, grid, s, h, a);
+  else if (fi == 4) launch_pass2_fi<D, 4>(dm, grid, s, h, a);
+  else launch_pass2_fi<D, kMaxFastItems>(dm, grid, s, h, a);
 }
 
 template <int D, bool SINGLE>
@@ -1391,15 +1399,17 @@ static void launch_pass1(const Pass1Args& a, int row_tiles, bool fold, uint32_t 
   if (a.seqs.nseq > 0) first_items = seq_items(seq_ranges(a.seqs.len[0], a.mode, a.W, a.S), a.C, nullptr) * a.Hkv;
   const int32_t L_first = a.seqs.nseq > 0 ? a.seqs.len[0] : 0;
   const int32_t mode_g_t = a.mode | (a.G << 8) | (a.T << 16);
-#define P1_HOT a.q, a.table, first_items, L_first, mode_g_t, a.W, a.S, a.C, a.Hq, a.max_blocks, a.num_blocks, a
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 64 * kWaves, lds, s>>>(a.q, a.table, first_items, L_first, mode_g_t, a.W, a.S, a.C, a.Hq,
+                                          a.max_blocks, a.num_blocks, a);
+  };
   if (row_tiles == 1) {
-    if (fold) pass1_kernel<D, 1, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
-    else pass1_kernel<D, 1, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
+    if (fold) go(pass1_kernel<D, 1, true, SINGLE>);
+    else go(pass1_kernel<D, 1, false, SINGLE>);
   } else {
-    if (fold) pass1_kernel<D, 2, true, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
-    else pass1_kernel<D, 2, false, SINGLE><<<grid, 64 * kWaves, lds, s>>>(P1_HOT);
+    if (fold) go(pass1_kernel<D, 2, true, SINGLE>);
+    else go(pass1_kernel<D, 2, false, SINGLE>);
   }
-#undef P1_HOT
 }
 
 }  // namespace da
@@ -1562,16 +1572,14 @@ static int decode_impl(const draft_attn_params* p, const void* q, const void* k_
     const int dm = !fused ? 0 : (draft_in_pass1 ? 1 : (a2.T <= 16 ? 16 : 32));
     // leading scalar arguments: record pointers, shape, and the first
     // sequence's item counts (from the launch's sequence table; -1 without one)
-    int32_t n_first = -1, nm_first = 0;
-    if (a2.seqs.nseq > 0) n_first = seq_items(seq_ranges(a2.seqs.len[0], a2.mode, a2.W, a2.S), a2.C, &nm_first);
-#define P2_HOT a2.stat, a2.acc, a2.R, a2.Hkv, a2.rows_pad, a2.total_items, n_first, nm_first
+    Pass2Lead h{a2.stat, a2.acc, a2.R, a2.Hkv, a2.rows_pad, a2.total_items, -1, 0};
+    if (a2.seqs.nseq > 0) h.n_first = seq_items(seq_ranges(a2.seqs.len[0], a2.mode, a2.W, a2.S), a2.C, &h.nm_first);
     // records each thread of the merge kernel loads in its one round
     const int32_t ng = 256 / (D / 4);
     const int32_t fi = pr.max_group_items <= ng ? 1 : pr.max_group_items <= 2 * ng ? 2
                      : pr.max_group_items <= 4 * ng ? 4 : kMaxFastItems;
-    if (D == 64) launch_pass2<64>(dm, fi, rows_total, s, P2_HOT, a2);
-    else launch_pass2<128>(dm, fi, rows_total, s, P2_HOT, a2);
-#undef P2_HOT
+    if (D == 64) launch_pass2<64>(dm, fi, rows_total, s, h, a2);
+    else launch_pass2<128>(dm, fi, rows_total, s, h, a2);
   }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
