@@ -373,6 +373,35 @@ def test_in_order_block_table_gives_identical_results():
             assert np.array_equal(a, b) and np.array_equal(la, lb), f"{kw} split={split}"
 
 
+def _permute_sequences(x, perm):
+    y = dict(x)
+    y["q"] = x["q"][perm]
+    y["block_table"] = x["block_table"][perm]
+    y["ctx_len"] = x["ctx_len"][perm]
+    y["ctx_lens"] = [x["ctx_lens"][i] for i in perm]
+    return y
+
+
+@pytest.mark.parametrize("lens,perm,launch", [
+    ([3000, 1234, 517, 0, 64], [2, 0, 4, 1, 3], "two_pass"),
+    ([3000, 1234, 517, 0, 64], [2, 0, 4, 1, 3], "single"),
+    ([300 + 37 * i for i in range(40)], list(range(39, -1, -1)), "two_pass"),
+], ids=["5seq-two_pass", "5seq-single", "40seq-two_pass"])
+def test_sequence_position_does_not_change_its_result(lens, perm, launch):
+    # The first sequence's workgroups start from preloaded kernel arguments, the
+    # others from the argument block, and beyond 32 sequences every workgroup
+    # finds its sequence from ctx_len on the device: a sequence's result is the
+    # same bits whatever its position in the batch.
+    x = synth.make_inputs(ctx_lens=lens, T=4, Hq=8, Hkv=2, d=128, seed=19, fold=True)
+    y = _permute_sequences(x, perm)
+    for kw in (dict(mode="full"), dict(mode="window", window=700, n_sink=4),
+               dict(mode="fold", window=900, alpha=2.0, beta=-1.0)):
+        a = run_gpu(to_dev(x), kw, launch=launch)
+        b = run_gpu(to_dev(y), kw, launch=launch)
+        assert np.array_equal(a[0][perm], b[0]) and np.array_equal(a[1][perm], b[1]), (kw, launch)
+        assert np.array_equal(a[2][perm], b[2]), (kw, launch)
+
+
 def test_deterministic_and_stream_safe():
     da = _da()
     x = synth.make_inputs(ctx_lens=[8000, 900], T=4, Hq=16, Hkv=4, d=128, seed=16, fold=True)
