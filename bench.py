@@ -398,27 +398,25 @@ def _event_mean_us(fn, steps, warmup):
     return a.elapsed_time(b) * 1e3 / steps, wall
 
 
-def bench_append(args):
-    """KV append (draft_attn_append) with the FOLD side cache. Cases: 'decode' writes the
-    accepted tokens of a draft step (16 sequences x 8 tokens at ragged positions); 'prefill'
-    writes a 64K-token chunk of one sequence. Algorithmic bytes per token and kv head: read
-    k_new and v_new, write the rotated key, the side key and the value, 10 * d bytes."""
-    import numpy as np
+def append_inputs(case, seed):
+    """Inputs of the KV append (draft_attn_append) with the FOLD side cache. Cases: 'decode'
+    writes the accepted tokens of a draft step (16 sequences x 8 tokens at ragged positions);
+    'prefill' writes a 64K-token chunk of one sequence. Algorithmic bytes per token and kv
+    head: read k_new and v_new, write the rotated key, the side key and the value, 10 * d
+    bytes."""
     import torch
 
-    import draft_attention_amd as da
     import synth
 
-    case = args.case or "prefill"
     Hkv, d = 8, 128
     if case == "decode":
-        pos = synth.ragged_lengths(16, 32768, 524288, args.seed)
+        pos = synth.ragged_lengths(16, 32768, 524288, seed)
         n_new = 8
     else:
         pos, n_new = [1000], 65536
     B = len(pos)
     dev = torch.device("cuda:0")
-    g = torch.Generator(device=dev).manual_seed(args.seed)
+    g = torch.Generator(device=dev).manual_seed(seed)
     spans = [list(range(p // 16, (p + n_new - 1) // 16 + 1)) for p in pos]
     MB = max(sp[-1] for sp in spans) + 1
     table = torch.full((B, MB), -1, dtype=torch.int32)
@@ -433,12 +431,28 @@ def bench_append(args):
     kn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
     vn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
     posd = torch.tensor(pos, dtype=torch.int32, device=dev)
+    return dict(pos=pos, n_new=n_new, B=B, Hkv=Hkv, d=d, table=table, kc=kc, vc=vc, ks=ks, kn=kn, vn=vn, posd=posd,
+                nbytes=B * n_new * Hkv * 10 * d)
 
-    call = da.prepare_append(kn, vn, table, posd, kc, vc, ks, rope="neox", rope_theta=5e5, pos_host=pos)
 
-    us, wall = _event_mean_us(call, args.steps, args.warmup)
-    nbytes = B * n_new * Hkv * 10 * d
-    gbs = nbytes / (us * 1e-6) / 1e9
+def time_append(case, steps, warmup, seed):
+    """Inputs, mean and wall µs per append call (HIP events around each call), GB/s."""
+    import draft_attention_amd as da
+
+    x = append_inputs(case, seed)
+    call = da.prepare_append(x["kn"], x["vn"], x["table"], x["posd"], x["kc"], x["vc"], x["ks"], rope="neox",
+                             rope_theta=5e5, pos_host=x["pos"])
+    us, wall = _event_mean_us(call, steps, warmup)
+    return x, us, wall, x["nbytes"] / (us * 1e-6) / 1e9
+
+
+def bench_append(args):
+    """KV append (draft_attn_append) with the FOLD side cache; cases as in append_inputs."""
+    case = args.case or "prefill"
+    x, us, wall, gbs = time_append(case, args.steps, args.warmup, args.seed)
+    pos, n_new, B, Hkv, d = x["pos"], x["n_new"], x["B"], x["Hkv"], x["d"]
+    table, kc, vc, ks, kn, vn = x["table"], x["kc"], x["vc"], x["ks"], x["kn"], x["vn"]
+    nbytes = x["nbytes"]
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -571,9 +585,11 @@ def secondary_rates(wl, args):
     and fraction of 8 TB/s: FULL at 128K; the windowed steps (window + sinks) at
     128K and 1M against their launch floor; FOLD at 256K for every alpha/beta pair
     of that workload; the 16-sequence ragged batch with query scaling, FULL and
-    FOLD; and the window steps with the step's draft tokens (fused and as two
-    calls). Inputs are generated once per workload; each entry warms up with the
-    run's W steps and then for at least 200 ms more before it is timed."""
+    FOLD; the window steps with the step's draft tokens (fused and as two
+    calls); and the KV append of a draft step's accepted tokens and of a 64K-token
+    prefill chunk. Inputs are generated once per workload; each decode entry
+    warms up with the run's W steps and then for at least 200 ms more before it
+    is timed."""
     import torch
 
     out = {}
@@ -602,6 +618,13 @@ def secondary_rates(wl, args):
         out[f"decode_draft/{case}"] = dict(fused_us=round(d["fused_us"], 2),
                                            two_calls_us=round(d["two_calls_us"], 2),
                                            draft_tokens=d["T"], window=d["W"], ctx_len=d["L"])
+    for case in ("decode", "prefill"):
+        x, us, _, gbs = time_append(case, steps, warmup, seed)
+        out[f"append/{case}"] = dict(us_per_call=round(us, 2), gbs=round(gbs, 1),
+                                     pct_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 2), num_seqs=x["B"],
+                                     num_new=x["n_new"], bytes=x["nbytes"])
+        del x
+        torch.cuda.empty_cache()
     return out
 
 
