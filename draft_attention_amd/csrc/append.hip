@@ -12,6 +12,7 @@
 // fp64 rotation that is within a few fp64 ulps of the exact one.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -19,6 +20,7 @@
 
 namespace da {
 
+constexpr int kAppendArgSeqs = 32;
 
 struct AppendArgs {
   const __bf16* k_new;  // [B][n_new][Hkv][D]
@@ -31,6 +33,8 @@ struct AppendArgs {
   uint32_t* status;     // optional device status word, or null
   int32_t B, n_new, Hkv, max_blocks, num_blocks, rope;
   int32_t span;         // logical blocks one sequence's append can touch
+  int32_t npos;         // B when B <= kAppendArgSeqs (positions below), else 0 (read pos)
+  int32_t pos_h[kAppendArgSeqs];  // the host copy of pos, for up to kAppendArgSeqs sequences
   double omega[64];     // rope_theta^(-2i/D)
   double cos_w[64];     // cos(omega_i), sin(omega_i): one position step
   double sin_w[64];
@@ -78,8 +82,23 @@ __device__ __forceinline__ void store_nt(T v, T* p) {
   else *p = v;
 }
 
+// The arguments the prologue reads (up to the end of pos_h) span a few 64-byte
+// lines of the scalar cache; each line's first read misses. Loading one word
+// of every line at entry, with independent loads and one wait, pays that miss
+// once instead of once per line in a chain of dependent reads.
+__device__ __forceinline__ void touch_append_args(const AppendArgs& a) {
+  constexpr int N = (int)((offsetof(AppendArgs, omega) + 63) / 64);
+  static_assert(N <= 4, "prologue arguments span at most four lines");
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(&a);
+  uint32_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = i < N ? p[16 * i] : 0u;
+  asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]));
+}
+
 template <int D, bool NT>
 __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  touch_append_args(a);
   constexpr int NO = D / 8;               // channel octets
   constexpr int HALF = D / 2;             // rotation pairs
   constexpr int SPT = 16 * HALF / 256;    // slots per thread in the rotation
@@ -96,7 +115,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   w /= a.Hkv;
   const int32_t jj = (int32_t)(w % a.span);
   const int32_t b = (int32_t)(w / a.span);
-  const int32_t p0 = a.pos[b];
+  // Up to 32 sequences take their position from the launch arguments, so the
+  // block-table and new-token loads do not wait for a read of pos first.
+  const int32_t p0 = a.npos > 0 ? a.pos_h[b] : a.pos[b];
   if (p0 < 0) return;
   const int32_t j = (p0 >> 4) + jj;
   const int64_t lo64 = (int64_t)j * 16 > p0 ? (int64_t)j * 16 : p0;
@@ -260,6 +281,8 @@ extern "C" int draft_attn_append(const draft_attn_append_params* p, const void* 
     for (double* t : {a.omega, a.cos_w, a.sin_w, a.cos_g, a.sin_g}) memset(t, 0, 64 * sizeof(double));  // unread
   }
   a.span = (p->num_new + 15) / 16 + 1;
+  a.npos = p->num_seqs <= kAppendArgSeqs ? p->num_seqs : 0;
+  for (int32_t b = 0; b < a.npos; ++b) a.pos_h[b] = pos_host[b];
   const uint32_t grid = (uint32_t)((int64_t)a.B * a.span * a.Hkv);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();

@@ -356,8 +356,10 @@ int draft_attn_decode_draft(const draft_attn_params* p, const void* q, const voi
  * The unrotated side cache is what FOLD's far memory reads ["FOLD: Position-Free
  * Far Memory with Local Order for Long-Context Speculative Decoding", review].
  * k_new, v_new: bf16 [B][num_new][Hkv][d] device, 16-byte aligned; pos_dev /
- * pos_host: int32 [B] on device / host with the same values; caches as for
- * draft_attn_decode. Every written block must be allocated in block_table; a
+ * pos_host: int32 [B] on device / host with the same values (for up to 32
+ * sequences the kernel takes the positions from pos_host, passed with the
+ * launch, so a captured call is bound to the host positions of the capture);
+ * caches as for draft_attn_decode. Every written block must be allocated in block_table; a
  * token whose table entry lies outside [0, num_blocks) is not written (and
  * sets DRAFT_ATTN_STATUS_APPEND_BAD_BLOCK in *status_flags when that is set). Nothing
  * outside the new tokens' slots is touched. Validation is host-side and runs
