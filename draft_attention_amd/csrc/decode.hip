@@ -51,6 +51,7 @@
 
 #include "draft_part.h"
 #include "host.h"
+#include "lanes.h"
 #include "plan.h"
 
 namespace da {
@@ -146,54 +147,8 @@ __device__ __forceinline__ void touch_args(const T& a) {
                "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]), "s"(v[12]), "s"(v[13]), "s"(v[14]), "s"(v[15]));
 }
 
-// ---------------------------------------------------------------- lane helpers
-// permlane16/32 swaps return the pair {x[l], x[l^16]} (resp. l^32) in the two halves.
-__device__ __forceinline__ float pair_max16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_max32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_add16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float pair_add32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+// 2^x on the transcendental unit (the cross-lane reductions are in lanes.h)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// All-lane reductions of a wave through the lane crossbars that need no LDS:
-// DPP quad permutations and row mirrors within each 16-lane row, then the
-// permlane16/32 swaps across rows. Every step combines a lane with a partner
-// that holds the mirror-image operand pair, so by commutativity every lane
-// ends with the same bits (rotations would leave the lanes of a row with sums
-// associated differently).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
-constexpr int kDppMirror = 0x140;      // row_mirror: lane i <-> 15 - i of its row
-constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7 - i of its half row
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_f<kDppXor1>(x));
-  x = fmaxf(x, dpp_f<kDppXor2>(x));
-  x = fmaxf(x, dpp_f<kDppMirror>(x));
-  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
-  return pair_max32(pair_max16(x));
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x += dpp_f<kDppXor1>(x);
-  x += dpp_f<kDppXor2>(x);
-  x += dpp_f<kDppMirror>(x);
-  x += dpp_f<kDppHalfMirror>(x);
-  return pair_add32(pair_add16(x));
-}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -23,55 +23,67 @@ namespace da {
 
 constexpr int kLenArgs = 32;
 
+// The arguments after the leading scalars (which the kernel receives preloaded
+// in scalar registers).
 struct MergeArgs {
-  const __bf16* q;   // [B][T][Hq][D]
-  const __bf16* kd;  // [B][T][Hkv][D], rotated at the draft positions
-  const __bf16* vd;  // [B][T][Hkv][D]
   const int32_t* ctx_len;
-  float* out;        // [B][T][Hq][D], in place
-  float* lse;        // [B][T][Hq], in place
-  int32_t B, T, Hq, Hkv, G, mode, W, S, n0;
+  int32_t mode, W, S, n0;
   float kappa, scale;
   // Lengths of a batch of up to kLenArgs sequences, from ctx_len_host, as
   // draft_attn_decode passes them: both calls then take the query scale's n
   // from the same source (larger batches read ctx_len in device memory).
-  int32_t nlen;            // B when B <= kLenArgs, else 0
   int32_t len[kLenArgs];
 };
 
-// One wave per (sequence, draft token, query head); lane l owns channels
-// l*CPL .. l*CPL + CPL - 1. Every load the wave needs (its query row, the cache
-// result, draft keys and values 0..t) is issued before any is used, so the call
-// costs about one memory round trip; the logits are then reduced across the
-// wave one draft key at a time (draft_part.h).
-template <int D, int TM>
-__global__ __launch_bounds__(64) void merge_draft_kernel(const MergeArgs a) {
+// One wave per (sequence b, draft token t, query head h) = (blockIdx.x, .y, .z);
+// lane l owns channels l*CPL .. l*CPL + CPL - 1. The sequence's length is read
+// first, then every load the wave needs (its query row, the cache result, draft
+// keys and values 0..t) is issued before any is used, so the call costs about
+// one memory round trip; the logits are then reduced across the wave
+// (draft_part.h). HOSTLEN: the length comes with the arguments.
+template <int D, int TM, bool HOSTLEN>
+__global__ __launch_bounds__(64) void merge_draft_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kd,
+                                                         const __bf16* __restrict__ vd, float* __restrict__ out,
+                                                         float* __restrict__ lse, int32_t T, int32_t Hq, int32_t Hkv,
+                                                         int32_t G, const MergeArgs a) {
   constexpr int CPL = D / 64;
   const int lane = threadIdx.x;
-  uint32_t r = blockIdx.x;  // grid = B * T * Hq < 2^31, checked on the host
-  const int32_t h = (int32_t)(r % (uint32_t)a.Hq);
-  r /= (uint32_t)a.Hq;
-  const int32_t t = (int32_t)(r % (uint32_t)a.T);
-  const int32_t b = (int32_t)(r / (uint32_t)a.T);
-  const int32_t kvh = h / a.G;
-  const int64_t qrow = ((int64_t)b * a.T + t) * a.Hq + h;
+  const int32_t b = blockIdx.x, t = blockIdx.y, h = blockIdx.z;
+  const int32_t L = HOSTLEN ? a.len[b] : a.ctx_len[b];
+  const int64_t qrow = ((int64_t)b * T + t) * Hq + h;
 
   DraftRow<D, TM> dr;
-  draft_row_load(dr, a.q, a.kd, a.vd, b, t, h, kvh, a.T, a.Hq, a.Hkv, lane);
+  draft_row_load(dr, q, kd, vd, b, t, h, h / G, T, Hq, Hkv, lane);
   float oc[CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) oc[e] = a.out[qrow * D + lane * CPL + e];
-  const float lse_c = a.lse[qrow];
-  const int32_t L = a.nlen > 0 ? a.len[b] : a.ctx_len[b];
+  for (int e = 0; e < CPL; ++e) oc[e] = out[qrow * D + lane * CPL + e];
+  const float lse_c = lse[qrow];
   const float c = draft_logit_scale(a.scale, a.kappa, visible_count(L, a.mode, a.W, a.S), a.n0);
   float lse_d, od[CPL];
   draft_row_part(dr, t, c, lse_d, od);
   const DraftMerge mg = draft_merge(lse_c, lse_d);
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    a.out[qrow * D + lane * CPL + e] = draft_merge_out(mg, oc[e], od[e]);
-  }
-  if (lane == 0) a.lse[qrow] = mg.lse;
+  for (int e = 0; e < CPL; ++e) out[qrow * D + lane * CPL + e] = draft_merge_out(mg, oc[e], od[e]);
+  if (lane == 0) lse[qrow] = mg.lse;
+}
+
+template <int D, int TM>
+static void launch_merge(bool hostlen, dim3 grid, hipStream_t s, const __bf16* q, const __bf16* kd,
+                         const __bf16* vd, float* out, float* lse, int32_t T, int32_t Hq, int32_t Hkv, int32_t G,
+                         const MergeArgs& a) {
+  if (hostlen) merge_draft_kernel<D, TM, true><<<grid, 64, 0, s>>>(q, kd, vd, out, lse, T, Hq, Hkv, G, a);
+  else merge_draft_kernel<D, TM, false><<<grid, 64, 0, s>>>(q, kd, vd, out, lse, T, Hq, Hkv, G, a);
+}
+
+// The kernel holds draft keys 0..TM-1 in registers: TM is the smallest of 8,
+// 16 and 32 that covers T.
+template <int D>
+static void launch_merge_d(bool hostlen, dim3 grid, hipStream_t s, const __bf16* q, const __bf16* kd,
+                           const __bf16* vd, float* out, float* lse, int32_t T, int32_t Hq, int32_t Hkv, int32_t G,
+                           const MergeArgs& a) {
+  if (T <= 8) launch_merge<D, 8>(hostlen, grid, s, q, kd, vd, out, lse, T, Hq, Hkv, G, a);
+  else if (T <= 16) launch_merge<D, 16>(hostlen, grid, s, q, kd, vd, out, lse, T, Hq, Hkv, G, a);
+  else launch_merge<D, 32>(hostlen, grid, s, q, kd, vd, out, lse, T, Hq, Hkv, G, a);
 }
 
 }  // namespace da
@@ -90,41 +102,27 @@ extern "C" int draft_attn_merge_draft(const draft_attn_params* p, const void* q,
   auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
   if (mis(q, 16) || mis(k_draft, 16) || mis(v_draft, 16) || mis(out, 8) || mis(lse, 4) || mis(ctx_len_dev, 4))
     return DRAFT_ATTN_EINVAL;
+  // grid (B, T, Hq): T <= DRAFT_ATTN_MAX_ROWS; the head count must fit the third dimension
+  if (p->num_q_heads > 65535) return DRAFT_ATTN_ENOTSUP;
   MergeArgs a;
-  a.q = (const __bf16*)q;
-  a.kd = (const __bf16*)k_draft;
-  a.vd = (const __bf16*)v_draft;
   a.ctx_len = ctx_len_dev;
-  a.out = out;
-  a.lse = lse;
-  a.B = p->num_seqs;
-  a.T = p->num_draft_tokens;
-  a.Hq = p->num_q_heads;
-  a.Hkv = p->num_kv_heads;
-  a.G = pr.G;
   a.mode = p->mode;
   a.W = p->window;
   a.S = p->n_sink;
   a.n0 = p->n0;
   a.kappa = p->kappa;
   a.scale = p->softmax_scale;
-  a.nlen = p->num_seqs <= kLenArgs ? p->num_seqs : 0;
-  for (int32_t b = 0; b < kLenArgs; ++b) a.len[b] = b < a.nlen ? ctx_len_host[b] : 0;
-  if ((int64_t)a.B * a.T * a.Hq > 0x7fffffff) return DRAFT_ATTN_EINVAL;
-  const uint32_t grid = (uint32_t)((int64_t)a.B * a.T * a.Hq);
+  const bool hostlen = p->num_seqs <= kLenArgs;
+  for (int32_t b = 0; b < kLenArgs; ++b) a.len[b] = hostlen && b < p->num_seqs ? ctx_len_host[b] : 0;
+  const dim3 grid((uint32_t)p->num_seqs, (uint32_t)p->num_draft_tokens, (uint32_t)p->num_q_heads);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
-  // The kernel holds draft keys 0..TM-1 in registers: TM is the smallest of 8,
-  // 16 and 32 that covers T.
-  if (p->head_dim == 64) {
-    if (a.T <= 8) merge_draft_kernel<64, 8><<<grid, 64, 0, s>>>(a);
-    else if (a.T <= 16) merge_draft_kernel<64, 16><<<grid, 64, 0, s>>>(a);
-    else merge_draft_kernel<64, 32><<<grid, 64, 0, s>>>(a);
-  } else {
-    if (a.T <= 8) merge_draft_kernel<128, 8><<<grid, 64, 0, s>>>(a);
-    else if (a.T <= 16) merge_draft_kernel<128, 16><<<grid, 64, 0, s>>>(a);
-    else merge_draft_kernel<128, 32><<<grid, 64, 0, s>>>(a);
-  }
+  auto* qb = (const __bf16*)q;
+  auto* kb = (const __bf16*)k_draft;
+  auto* vb = (const __bf16*)v_draft;
+  const int32_t T = p->num_draft_tokens, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  if (p->head_dim == 64) launch_merge_d<64>(hostlen, grid, s, qb, kb, vb, out, lse, T, Hq, Hkv, pr.G, a);
+  else launch_merge_d<128>(hostlen, grid, s, qb, kb, vb, out, lse, T, Hq, Hkv, pr.G, a);
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;
 }

@@ -23,6 +23,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "lanes.h"
+
 namespace da {
 
 template <int D, int TM>
@@ -31,12 +33,6 @@ struct DraftRow {
   float qv[CPL];
   __bf16 kx[TM][CPL], vx[TM][CPL];
 };
-
-__device__ __forceinline__ float draft_wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
 
 // Loads of row (b, t, h): the query row and draft keys/values 0..TM-1 of kv
 // head kvh. Every load is unconditional, from draft token min(j, t), so that
@@ -49,36 +45,48 @@ __device__ __forceinline__ void draft_row_load(DraftRow<D, TM>& r, const __bf16*
   const int64_t qrow = ((int64_t)b * T + t) * Hq + h;
 #pragma unroll
   for (int e = 0; e < CPL; ++e) r.qv[e] = (float)q[qrow * D + lane * CPL + e];
+  // draft token 0 of (b, kvh); consecutive draft tokens are Hkv * D elements apart
+  const int64_t row0 = ((int64_t)b * T * Hkv + kvh) * D + lane * CPL;
+  const __bf16* kp = kd + row0;
+  const __bf16* vp = vd + row0;
+  const int64_t stride = (int64_t)Hkv * D;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int32_t jc = j <= t ? j : t;
-    const int64_t row = (((int64_t)b * T + jc) * Hkv + kvh) * D + lane * CPL;
+    const int64_t off = (j <= t ? j : t) * stride;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
-      r.kx[j][e] = kd[row + e];
-      r.vx[j][e] = vd[row + e];
+      r.kx[j][e] = kp[off + e];
+      r.vx[j][e] = vp[off + e];
     }
   }
 }
 
 // The draft part of the row: lse_d and the normalised out_d channels of this
-// lane. c: logit scale (natural-log domain).
+// lane. c: logit scale (natural-log domain). The TM dot products are formed and
+// reduced across the wave (lanes.h) for every held key, with no branch between
+// them, so that their reductions overlap; keys j > t (loaded from draft token
+// t) are then masked.
 template <int D, int TM>
 __device__ __forceinline__ void draft_row_part(const DraftRow<D, TM>& r, int32_t t, float c, float& lse_d,
                                                float (&od)[D / 64]) {
+  // no multiply-add contraction, so that every kernel that inlines this rounds alike
+#pragma clang fp contract(off)
   constexpr int CPL = D / 64;
   float lg[TM];
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) part = fmaf(r.qv[e], (float)r.kx[j][e], part);
+    lg[j] = part;
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) lg[j] = wave_sum(lg[j]);
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    lg[j] = -INFINITY;
-    if (j <= t) {
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) part = fmaf(r.qv[e], (float)r.kx[j][e], part);
-      lg[j] = c * draft_wave_sum(part);
-      m = fmaxf(m, lg[j]);
-    }
+    lg[j] = j <= t ? c * lg[j] : -INFINITY;
+    m = fmaxf(m, lg[j]);
   }
   float z = 0.f;
 #pragma unroll
@@ -117,7 +125,10 @@ __device__ __forceinline__ float draft_merge_out(const DraftMerge& mg, float out
 }
 
 // Logit scale of the draft part for a sequence with n cached visible keys.
+// With kappa = 0, s(n) is exactly 1 (n / n0 >= 1, so its logarithm is finite),
+// and the logarithm is skipped.
 __device__ __forceinline__ float draft_logit_scale(float scale, float kappa, int32_t n, int32_t n0) {
+  if (kappa == 0.f) return scale;
   const double sn = 1.0 + (double)kappa * log((double)(n > n0 ? n : n0) / (double)n0);
   return (float)((double)scale * sn);
 }

@@ -456,6 +456,16 @@ def test_merge_draft_refuses_bf16_output():
     assert st == -4
 
 
+def test_merge_draft_refuses_more_query_heads_than_its_grid_spans():
+    # one grid dimension of the merge kernel spans the query heads (at most
+    # 65535); refused on the host, before anything is enqueued
+    host = (ctypes.c_int32 * 2)(*LENS)
+    p = params(num_q_heads=65536, num_kv_heads=8192, num_draft_tokens=1)
+    st = da().lib.draft_attn_merge_draft(ctypes.byref(p), 0x10000, 0x20000, 0x30000, 0x60000, host, 0x70000,
+                                         0x80000, None)
+    assert st == -4
+
+
 def test_fused_decode_draft_validates_the_draft_pointers():
     # Checked on the host before anything is enqueued (no GPU needed): both
     # draft pointers are required and must be 16-byte aligned.

@@ -112,3 +112,37 @@ def test_fused_decode_draft_equals_the_two_calls(kw, d, T, G):
                        k_draft=kd, v_draft=vd, **kw)
     torch.cuda.synchronize()
     assert torch.equal(bo, out.to(torch.bfloat16)) and torch.equal(bl, lse)
+
+
+@pytest.mark.parametrize("kw", [dict(mode="full", kappa=0.1, n0=64), dict(mode="window", window=200, n_sink=4)],
+                         ids=["full-kappa", "window"])
+def test_draft_merge_of_a_batch_beyond_the_argument_lengths(kw):
+    # 40 sequences: more than the 32 whose lengths travel with the kernel
+    # arguments, so both the separate merge and the fused call read ctx_len in
+    # device memory. Checked against the oracle, and fused against two calls.
+    import draft_attention_amd as da
+    dev = torch.device("cuda:0")
+    rnd = np.random.default_rng(81)
+    lens = [int(v) for v in rnd.integers(0, 700, size=40)]
+    lens[3] = 0
+    B, T, Hkv, G, d = len(lens), 3, 2, 2, 64
+    x = synth.make_inputs(ctx_lens=lens, T=T, Hq=G * Hkv, Hkv=Hkv, d=d, seed=82)
+    g = torch.Generator().manual_seed(83)
+    kd = (torch.randn((B, T, Hkv, d), generator=g) * 2).to(torch.bfloat16)
+    vd = torch.randn((B, T, Hkv, d), generator=g).to(torch.bfloat16)
+    q, kc, vc = (x[k].to(dev) for k in ("q", "k_cache", "v_cache"))
+    table, ctx = x["block_table"].to(dev), x["ctx_len"].to(dev)
+    out, lse = da.decode(q, kc, vc, table, ctx, ctx_lens=lens, launch="two_pass", **kw)
+    da.merge_draft(q, kd.to(dev), vd.to(dev), ctx, out, lse, num_blocks=kc.shape[0],
+                   max_blocks_per_seq=table.shape[1], num_kv_heads=Hkv, ctx_lens=lens, **kw)
+    fo, fl = da.decode(q, kc, vc, table, ctx, ctx_lens=lens, k_draft=kd.to(dev), v_draft=vd.to(dev), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(fo, out) and torch.equal(fl, lse)
+    n = {k: (v.float().numpy() if torch.is_tensor(v) and v.is_floating_point() else v) for k, v in x.items()}
+    ref = oracle.decode_with_draft(n["q"], n["k_cache"], n["v_cache"], x["block_table"].numpy(), lens, kw["mode"],
+                                   kd.float().numpy(), vd.float().numpy(),
+                                   **{k: v for k, v in kw.items() if k != "mode"})
+    dout = float(np.abs(out.cpu().numpy() - ref["out"]).max())
+    dlse = float(np.abs(lse.cpu().numpy() - ref["lse"]).max())
+    print(f"merge_draft batch of {B} {kw}: max|dout|={dout:.3e} max|dlse|={dlse:.3e}", flush=True)
+    assert dout <= 1e-2 and dlse <= 1e-3
