@@ -45,7 +45,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["draft_attention_amd/csrc/decode.hip", "draft_attention_amd/csrc/plan.h"]
+KERNEL_SOURCES = ["draft_attention_amd/csrc/decode.hip", "draft_attention_amd/csrc/plan.h",
+                  "draft_attention_amd/csrc/lanes.h", "draft_attention_amd/csrc/draft_part.h"]
 
 
 def parse():
