@@ -212,7 +212,8 @@ def time_workload(w, kw, steps, warmup, seed, split, want_events=True, graph=Fal
             ev.destroy(b)
     floors = None
     if floor:
-        # The same eager loop over the call's launch shape with empty kernels.
+        # The same eager loop over the call's launch shape with empty kernels
+        # that take the real kernels' argument blocks.
         floors = {}
         for nk in (1, 2):
             fcall = da.prepare_launch_floor(p, w.ctx_lens, nk)
@@ -304,8 +305,8 @@ def rate_entry(r):
         floor = f2 if r["launch"] == "two_pass" else f1
         e.update(floor_one_kernel_us=round(f1, 2), floor_two_kernels_us=round(f2, 2),
                  above_floor_us=round(step - floor, 2),
-                 floor_note="the call's launch shape with empty kernels, same eager loop; above_floor "
-                            "is the step minus the floor of its own kernel count")
+                 floor_note="the call's launch shape (grids, LDS, argument block sizes) with empty kernels, "
+                            "same eager loop; above_floor is the step minus the floor of its own kernel count")
     return e
 
 

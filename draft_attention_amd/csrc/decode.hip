@@ -1591,8 +1591,14 @@ extern "C" int draft_attn_decode_noalloc(const draft_attn_params* p, const void*
 }
 
 namespace da {
-// Launch-floor kernel of draft_attn_launch_floor: it does nothing.
-__global__ __launch_bounds__(256) void empty_kernel() {}
+// Launch-floor kernels of draft_attn_launch_floor: they do nothing, and take
+// argument blocks of the same layout and size as pass 1 and pass 2, since the
+// runtime's cost of enqueueing a launch grows with its argument block.
+__global__ __launch_bounds__(256) void empty_pass1_kernel(const __bf16*, const int32_t*, int32_t, int32_t, int32_t,
+                                                          int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
+                                                          const Pass1Args) {}
+__global__ __launch_bounds__(256) void empty_pass2_kernel(const float4*, const float*, int32_t, int32_t, int32_t,
+                                                          int32_t, int32_t, int32_t, const Pass2Args) {}
 }  // namespace da
 
 extern "C" int draft_attn_launch_floor(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t kernels,
@@ -1605,10 +1611,14 @@ extern "C" int draft_attn_launch_floor(const draft_attn_params* p, const int32_t
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const size_t lds = da::pass1_lds_bytes(pr.chunk, pr.rows_pad, p->head_dim);
-  da::empty_kernel<<<(uint32_t)pr.total_items, 256, lds, s>>>();
+  da::Pass1Args a1;
+  da::Pass2Args a2;
+  memset(&a1, 0, sizeof a1);
+  memset(&a2, 0, sizeof a2);
+  da::empty_pass1_kernel<<<(uint32_t)pr.total_items, 256, lds, s>>>(nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, a1);
   if (kernels == 2) {
     const uint32_t rows_total = (uint32_t)((int64_t)p->num_seqs * p->num_kv_heads * pr.rows);
-    da::empty_kernel<<<rows_total, 256, 0, s>>>();
+    da::empty_pass2_kernel<<<rows_total, 256, 0, s>>>(nullptr, nullptr, 0, 0, 0, 0, 0, 0, a2);
   }
   if (hipGetLastError() != hipSuccess) return DRAFT_ATTN_EHIP;
   return DRAFT_ATTN_OK;

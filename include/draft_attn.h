@@ -282,9 +282,12 @@ int draft_attn_decode_noalloc(const draft_attn_params* p, const void* q, const v
  * to a constant], so its time is mostly fixed cost. This enqueues the launch
  * shape draft_attn_decode would use for these params and lengths with kernels
  * that do nothing: with kernels = 1, one kernel with the streaming pass's grid,
- * workgroup size and LDS; with kernels = 2, that kernel and then one with the
- * merge pass's grid. The time of such a step is the launch floor under the
- * decode call. Validation as for draft_attn_decode; kernels must be 1 or 2. */
+ * workgroup size, LDS and argument block; with kernels = 2, that kernel and
+ * then one with the merge pass's grid and argument block. (The runtime's cost
+ * of enqueueing a launch grows with the size of its argument block, so empty
+ * kernels without arguments would understate it.) The time of such a step is
+ * the launch floor under the decode call. Validation as for draft_attn_decode;
+ * kernels must be 1 or 2. */
 int draft_attn_launch_floor(const draft_attn_params* p, const int32_t* ctx_len_host, int32_t kernels,
                             void* stream);
 
