@@ -102,8 +102,9 @@ extern "C" int draft_attn_merge_draft(const draft_attn_params* p, const void* q,
   auto mis = [](const void* ptr, uintptr_t al) { return ((uintptr_t)ptr & (al - 1)) != 0; };
   if (mis(q, 16) || mis(k_draft, 16) || mis(v_draft, 16) || mis(out, 8) || mis(lse, 4) || mis(ctx_len_dev, 4))
     return DRAFT_ATTN_EINVAL;
-  // grid (B, T, Hq): T <= DRAFT_ATTN_MAX_ROWS; the head count must fit the third dimension
-  if (p->num_q_heads > 65535) return DRAFT_ATTN_ENOTSUP;
+  // grid (B, T, Hq) of 64-thread workgroups: T <= DRAFT_ATTN_MAX_ROWS; the
+  // head count must fit the third dimension, and B * 64 threads the first
+  if (p->num_q_heads > 65535 || (int64_t)p->num_seqs * 64 > 0xffffffffLL) return DRAFT_ATTN_ENOTSUP;
   MergeArgs a;
   a.ctx_len = ctx_len_dev;
   a.mode = p->mode;

@@ -324,8 +324,9 @@ int draft_attn_plan(const draft_attn_params* p, const int32_t* ctx_len_host, int
  * rotated at positions L_b + t) and v_draft: bf16 [B][T][Hkv][d]; out, lse: as
  * written by draft_attn_decode. p, ctx_len_dev and ctx_len_host: as for that call.
  * The merge needs the fp32 cache result: out_dtype DRAFT_ATTN_OUT_BF16 returns
- * DRAFT_ATTN_ENOTSUP, as does num_q_heads above 65535 (one grid dimension of
- * the merge kernel spans the query heads). */
+ * DRAFT_ATTN_ENOTSUP, as do num_q_heads above 65535 and num_seqs above 2^26
+ * (the merge kernel's grid spans the query heads in one dimension and the
+ * sequences, 64 threads each, in another). */
 int draft_attn_merge_draft(const draft_attn_params* p, const void* q, const void* k_draft, const void* v_draft,
                            const int32_t* ctx_len_dev, const int32_t* ctx_len_host, float* out, float* lse,
                            void* stream);
