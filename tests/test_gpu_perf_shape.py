@@ -52,3 +52,32 @@ def test_fold_step_costs_about_a_full_step():
     fold = step_us(L, dict(mode="fold", window=4096, alpha=2.0, beta=-1.0), T=6, fold=True)
     print(f"256K, 6 draft tokens: FULL {full:.1f} us, FOLD {fold:.1f} us", flush=True)
     assert 0.8 * full <= fold <= 1.25 * full
+
+
+def test_launch_floor_runs_the_call_shape_and_stays_below_the_step():
+    # draft_attn_launch_floor enqueues the decode call's launches (grids, LDS,
+    # argument blocks) with empty kernels; on one or two kernels it must run
+    # cleanly, and a real window step must not be cheaper than its own floor
+    # by more than noise
+    import draft_attention_amd as da
+    L, W = 1 << 17, 2048
+    p = da.make_params(num_seqs=1, num_draft_tokens=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       num_blocks=(L >> 4) + 16, max_blocks_per_seq=(L >> 4) + 8, mode="window", window=W,
+                       n_sink=4)
+    floors = {}
+    for nk in (1, 2):
+        call = da.prepare_launch_floor(p, [L], nk)
+        for _ in range(5):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(30):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        floors[nk] = a.elapsed_time(b) * 1e3 / 30
+    step = step_us(L, dict(mode="window", window=W, n_sink=4))
+    print(f"floor one kernel {floors[1]:.2f} us, two {floors[2]:.2f} us; window step {step:.2f} us", flush=True)
+    assert floors[1] > 0 and floors[2] > 0
+    assert step > 0.8 * floors[2]
