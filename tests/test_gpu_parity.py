@@ -439,6 +439,29 @@ def _full_size_inputs(w, seed=0):
                              fold=w.fold, needle_frac=w.needle_frac)
 
 
+def _head_subcache(w, kw, x, g, bsel):
+    """fp32 host copies of just kv head g's blocks that hold visible keys of the
+    sequences bsel, with their table rows renumbered to the copy."""
+    G = w.Hq // w.Hkv
+    table = x["block_table"].cpu()
+    rows = table[bsel].clone()
+    for i, b in enumerate(bsel):
+        main, far = oracle.index_sets(w.ctx_lens[b], kw["mode"], kw.get("window", 0), kw.get("n_sink", 0))
+        read = np.zeros(rows.shape[1], dtype=bool)
+        read[np.concatenate([main, far]) // 16] = True
+        rows[i, torch.from_numpy(~read)] = -1
+    used = torch.unique(rows[rows >= 0])
+    remap = torch.full((int(table.max()) + 1,), -1, dtype=torch.int64)
+    remap[used.long()] = torch.arange(used.numel())
+    sub_table = np.where(rows.numpy() >= 0, remap[rows.clamp(min=0).long()].numpy(), -1)
+    idx = used.long().to(x["k_cache"].device)
+    sub = dict(q=x["q"][bsel][:, :, g * G:(g + 1) * G].float().cpu().numpy(),
+               k=x["k_cache"][idx, g:g + 1].float().cpu().numpy(),
+               v=x["v_cache"][idx, g:g + 1].float().cpu().numpy(),
+               ks=None if x["k_side"] is None else x["k_side"][idx, g:g + 1].float().cpu().numpy())
+    return sub, sub_table
+
+
 def _sampled(w, kw, pairs, x=None, seed=0):
     """Full-size inputs generated on the GPU (or given); the GPU call runs in the
     launch configuration the bench times, on every sequence and head; the oracle
@@ -450,26 +473,9 @@ def _sampled(w, kw, pairs, x=None, seed=0):
     assert np.array_equal(vis, want)
     heads = sorted({g for _, g in pairs})
     G = w.Hq // w.Hkv
-    table = x["block_table"].cpu()
     for g in heads:
         bsel = sorted({b for b, gg in pairs if gg == g})
-        # fp32 host copies of just this head's blocks that hold visible keys of
-        # the selected sequences, with their table rows renumbered to the copy
-        rows = table[bsel].clone()
-        for i, b in enumerate(bsel):
-            main, far = oracle.index_sets(w.ctx_lens[b], kw["mode"], kw.get("window", 0), kw.get("n_sink", 0))
-            read = np.zeros(rows.shape[1], dtype=bool)
-            read[np.concatenate([main, far]) // 16] = True
-            rows[i, torch.from_numpy(~read)] = -1
-        used = torch.unique(rows[rows >= 0])
-        remap = torch.full((int(table.max()) + 1,), -1, dtype=torch.int64)
-        remap[used.long()] = torch.arange(used.numel())
-        sub_table = np.where(rows.numpy() >= 0, remap[rows.clamp(min=0).long()].numpy(), -1)
-        idx = used.long().to(x["k_cache"].device)
-        sub = dict(q=x["q"][bsel][:, :, g * G:(g + 1) * G].float().cpu().numpy(),
-                   k=x["k_cache"][idx, g:g + 1].float().cpu().numpy(),
-                   v=x["v_cache"][idx, g:g + 1].float().cpu().numpy(),
-                   ks=None if x["k_side"] is None else x["k_side"][idx, g:g + 1].float().cpu().numpy())
+        sub, sub_table = _head_subcache(w, kw, x, g, bsel)
         ref = oracle.decode(sub["q"], sub["k"], sub["v"], sub_table, [w.ctx_lens[b] for b in bsel],
                             k_side=sub["ks"], rope_theta=w.rope_theta, **kw)
         o = out[:, :, g * G:(g + 1) * G][bsel]
@@ -490,6 +496,39 @@ def test_full_size_needles_1m():
     x = _full_size_inputs(w)
     for kw in w.runs:
         _sampled(w, kw, pairs=[(0, g) for g in range(w.Hkv)], x=x)
+
+
+@pytest.mark.parametrize("name", ["llama8b_128k", "needles_1m"])
+def test_full_size_fused_window_draft_step(name):
+    # the window step of the workload with the step's draft keys, as one fused
+    # call (the shape bench.py's draft-step entries time): every kv head against
+    # the oracle's single softmax over the window, the sinks and draft keys 0..t,
+    # and the fused result equal to decode + merge_draft bit for bit
+    da = _da()
+    w = synth.workloads()[name]
+    kw = [r for r in w.runs if r["mode"] == "window"][0]
+    x = _full_size_inputs(w)
+    B = len(w.ctx_lens)
+    gen = torch.Generator(device="cuda:0").manual_seed(91)
+    kd = (torch.randn((B, w.T, w.Hkv, w.d), generator=gen, device="cuda:0") * 2).to(torch.bfloat16)
+    vd = torch.randn((B, w.T, w.Hkv, w.d), generator=gen, device="cuda:0").to(torch.bfloat16)
+    fo, fl = da.decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], ctx_lens=x["ctx_lens"],
+                       k_draft=kd, v_draft=vd, **kw)
+    o2, l2 = da.decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], ctx_lens=x["ctx_lens"],
+                       launch="two_pass", **kw)
+    da.merge_draft(x["q"], kd, vd, x["ctx_len"], o2, l2, num_blocks=x["k_cache"].shape[0],
+                   max_blocks_per_seq=x["block_table"].shape[1], num_kv_heads=w.Hkv, ctx_lens=x["ctx_lens"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(fo, o2) and torch.equal(fl, l2)
+    out, lse = fo.cpu().numpy(), fl.cpu().numpy()
+    G = w.Hq // w.Hkv
+    bsel = list(range(B))
+    for g in range(w.Hkv):
+        sub, sub_table = _head_subcache(w, kw, x, g, bsel)
+        ref = oracle.decode_with_draft(sub["q"], sub["k"], sub["v"], sub_table, w.ctx_lens, kw["mode"],
+                                       kd[:, :, g:g + 1].float().cpu().numpy(), vd[:, :, g:g + 1].float().cpu().numpy(),
+                                       **{k: v for k, v in kw.items() if k != "mode"})
+        compare(out[:, :, g * G:(g + 1) * G], lse[:, :, g * G:(g + 1) * G], ref, f"{name} fused {kw} kv={g}")
 
 
 def test_full_size_fold_256k():
