@@ -498,26 +498,29 @@ def test_full_size_needles_1m():
         _sampled(w, kw, pairs=[(0, g) for g in range(w.Hkv)], x=x)
 
 
-@pytest.mark.parametrize("name", ["llama8b_128k", "needles_1m"])
-def test_full_size_fused_window_draft_step(name):
-    # the window step of the workload with the step's draft keys, as one fused
-    # call (the shape bench.py's draft-step entries time): every kv head against
-    # the oracle's single softmax over the window, the sinks and draft keys 0..t,
-    # and the fused result equal to decode + merge_draft bit for bit
+@pytest.mark.parametrize("name,run", [("llama8b_128k", 1), ("needles_1m", 1), ("fold_256k", 3)])
+def test_full_size_fused_draft_step(name, run):
+    # a step of the workload with the step's draft keys, as one fused call (the
+    # window steps are the shape bench.py's draft-step entries time; FOLD at
+    # alpha = 2, beta = -1): every kv head against the oracle's single softmax
+    # over the step's keys and draft keys 0..t, and the fused result equal to
+    # decode + merge_draft bit for bit
     da = _da()
     w = synth.workloads()[name]
-    kw = [r for r in w.runs if r["mode"] == "window"][0]
+    kw = w.runs[run]
     x = _full_size_inputs(w)
+    side = x["k_side"] if kw["mode"] == "fold" else None
     B = len(w.ctx_lens)
     gen = torch.Generator(device="cuda:0").manual_seed(91)
     kd = (torch.randn((B, w.T, w.Hkv, w.d), generator=gen, device="cuda:0") * 2).to(torch.bfloat16)
     vd = torch.randn((B, w.T, w.Hkv, w.d), generator=gen, device="cuda:0").to(torch.bfloat16)
     fo, fl = da.decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], ctx_lens=x["ctx_lens"],
-                       k_draft=kd, v_draft=vd, **kw)
+                       k_side=side, rope_theta=w.rope_theta, k_draft=kd, v_draft=vd, **kw)
     o2, l2 = da.decode(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["ctx_len"], ctx_lens=x["ctx_lens"],
-                       launch="two_pass", **kw)
+                       k_side=side, rope_theta=w.rope_theta, launch="two_pass", **kw)
     da.merge_draft(x["q"], kd, vd, x["ctx_len"], o2, l2, num_blocks=x["k_cache"].shape[0],
-                   max_blocks_per_seq=x["block_table"].shape[1], num_kv_heads=w.Hkv, ctx_lens=x["ctx_lens"], **kw)
+                   max_blocks_per_seq=x["block_table"].shape[1], num_kv_heads=w.Hkv, ctx_lens=x["ctx_lens"],
+                   rope_theta=w.rope_theta, **kw)
     torch.cuda.synchronize()
     assert torch.equal(fo, o2) and torch.equal(fl, l2)
     out, lse = fo.cpu().numpy(), fl.cpu().numpy()
@@ -527,6 +530,7 @@ def test_full_size_fused_window_draft_step(name):
         sub, sub_table = _head_subcache(w, kw, x, g, bsel)
         ref = oracle.decode_with_draft(sub["q"], sub["k"], sub["v"], sub_table, w.ctx_lens, kw["mode"],
                                        kd[:, :, g:g + 1].float().cpu().numpy(), vd[:, :, g:g + 1].float().cpu().numpy(),
+                                       k_side=sub["ks"], rope_theta=w.rope_theta,
                                        **{k: v for k, v in kw.items() if k != "mode"})
         compare(out[:, :, g * G:(g + 1) * G], lse[:, :, g * G:(g + 1) * G], ref, f"{name} fused {kw} kv={g}")
 
