@@ -232,3 +232,46 @@ def test_large_append_streaming_path_matches_oracle(d, n_new):
             m = ~np.isnan(ref)
             assert int(m.sum()) == 1000 * Hkv * d
             assert np.array_equal(ref[m], got[m])
+
+
+@pytest.mark.parametrize("case", ["decode", "prefill"])
+def test_bench_append_cases_match_the_oracle(case):
+    # The append exactly as bench.py times it (its inputs and a prepared call):
+    # the decode-time case (16 sequences x 8 accepted tokens at ragged
+    # positions, 8 kv heads, d = 128) checked on every written slot, the
+    # 64K-token prefill on 512 tokens at each end of the chunk; bit for bit.
+    import bench
+    da = _da()
+    x = bench.append_inputs(case, 0)
+    call = da.prepare_append(x["kn"], x["vn"], x["table"], x["posd"], x["kc"], x["vc"], x["ks"], rope="neox",
+                             rope_theta=5e5, pos_host=x["pos"])
+    call()
+    torch.cuda.synchronize()
+    tab = x["table"].cpu().numpy()
+    n_new, B, Hkv, d = x["n_new"], x["B"], x["Hkv"], x["d"]
+    windows = [(0, n_new)] if case == "decode" else [(0, 512), (n_new - 512, n_new)]
+    for a, e in windows:
+        # the physical blocks the window writes, as a compact pool with its own table
+        logical = sorted({(b, (x["pos"][b] + i) // 16) for b in range(B) for i in range(a, e)})
+        phys = [int(tab[b, j]) for b, j in logical]
+        sub_tab = np.full(tab.shape, -1, dtype=np.int64)
+        for k, (b, j) in enumerate(logical):
+            sub_tab[b, j] = k
+        idx = torch.tensor(phys, dtype=torch.long, device=x["kc"].device)
+        got = [_np(t[idx]) for t in (x["kc"], x["vc"], x["ks"])]
+        zk = np.zeros((len(phys), Hkv, d // 8, 16, 8))
+        zv = np.zeros((len(phys), Hkv, d, 16))
+        ref = oracle.append(_np(x["kn"][:, a:e]), _np(x["vn"][:, a:e]), sub_tab, [p + a for p in x["pos"]],
+                            zk, zv, zk.copy(), rope="neox", rope_theta=5e5)
+        # compare the slots the window writes
+        mask_k = np.zeros(zk.shape, dtype=bool)
+        mask_v = np.zeros(zv.shape, dtype=bool)
+        for b in range(B):
+            for i in range(a, e):
+                p = x["pos"][b] + i
+                k = int(sub_tab[b, p // 16])
+                mask_k[k, :, :, p % 16, :] = True
+                mask_v[k, :, :, p % 16] = True
+        for r, g, m in zip(ref, got, (mask_k, mask_v, mask_k)):
+            assert int(m.sum()) == B * (e - a) * Hkv * d
+            assert np.array_equal(r[m], g[m]), (case, a, e)
